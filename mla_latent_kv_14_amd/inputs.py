@@ -1,0 +1,190 @@
+"""Seeded synthetic workloads for absorbed MLA decode over a paged latent cache.
+
+This module only draws numbers and lays them out; it performs none of the
+attention arithmetic.  It is the one piece shared by the HIP path (tests,
+bench) and the CPU oracle, which both receive the arrays it returns.
+
+Shapes follow DeepSeek-V2/V3 attention: n_h = 128 heads, per-head content
+width d_h = 128, KV latent width d_c = 512 and decoupled RoPE width 64
+("DeepSeek-V2 Multi-Head Latent Attention" knowledge note, Query Compression
+table; "DeepSeek-V3 MLA: Multi-Head Latent Attention Guide", Core
+Architecture section 1).  Every cache row holds ``[c_kv (d_c) | k_rope
+(d_rope)]``, the two quantities that page's cache rule keeps per token.
+
+Recipe:
+  * one ``numpy.random.Generator(PCG64(seed))`` per problem, draws in the
+    order: lengths, block permutation, cache, q_nope, q_rope, W_UK, W_UV;
+  * values are drawn in float64, cast to float32 and, for bf16 problems,
+    rounded once to bf16 (round-to-nearest-even through torch);
+  * latents, rope keys and queries ~ N(0, 1); W_UK and W_UV ~ N(0, 1)/sqrt(d_c)
+    (d_c is the fan-in of k = W c);
+  * the paged pool holds exactly sum_b ceil(L_b / bs) blocks whose physical
+    order is a random permutation; table rows are padded with -1;
+  * cache slots past a sequence's length in its last block are poisoned
+    (NaN by default) because nothing may read them.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "Problem", "make_problem", "workload"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """A named decode workload: dimensions plus the length distribution."""
+
+    name: str
+    dtype: str  # "f32" or "bf16": storage type of q, cache and weights
+    batch: int
+    heads: int
+    d_c: int
+    d_rope: int
+    d_nope: int
+    d_v: int
+    q_len: int
+    block_size: int
+    lengths: tuple  # ("fixed", (L0, L1, ...)) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
+    seed_base: int
+
+    @property
+    def row_width(self) -> int:
+        return self.d_c + self.d_rope
+
+    @property
+    def scale(self) -> float:
+        # softmax scale 1/sqrt(d_nope + d_rope); the caller always passes it
+        return 1.0 / math.sqrt(self.d_nope + self.d_rope)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_f32", "f32", 2, 8, 64, 16, 32, 32, 1, 16, ("fixed", (37, 200)), 1000),
+        Workload("single_4k_bf16", "bf16", 1, 128, 512, 64, 128, 128, 1, 64, ("fixed", (4096,)), 2000),
+        Workload("batch64_1k8k_bf16", "bf16", 64, 128, 512, 64, 128, 128, 1, 64, ("uniform", 1024, 8192), 3000),
+        Workload("long128k_bf16", "bf16", 4, 128, 512, 64, 128, 128, 1, 64, ("fixed", (131072,) * 4), 4000),
+        Workload("mtp2_lognormal_bf16", "bf16", 128, 16, 512, 64, 128, 128, 2, 64,
+                 ("lognormal", 2048, 1.0, 64, 32768), 5000),
+    ]
+}
+
+
+def workload(name: str, **overrides) -> Workload:
+    """Return a named workload, optionally with fields replaced (smaller test sizes)."""
+    return dataclasses.replace(WORKLOADS[name], **overrides)
+
+
+@dataclasses.dataclass
+class Problem:
+    """One drawn problem.  Tensors live on the CPU in the storage dtype."""
+
+    wl: Workload
+    seed: int
+    seq_lens: np.ndarray  # int32 [B]
+    block_table: np.ndarray  # int32 [B, MB], -1 padded
+    cache: torch.Tensor  # [NB, bs, d_c + d_rope]
+    q_nope: torch.Tensor  # [B, Lq, H, d_nope]
+    q_rope: torch.Tensor  # [B, Lq, H, d_rope]
+    w_uk: torch.Tensor  # [H, d_nope, d_c]
+    w_uv: torch.Tensor  # [H, d_v, d_c]
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.cache.shape[0])
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def scale(self) -> float:
+        return self.wl.scale
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum())
+
+    def f64(self, name: str) -> np.ndarray:
+        """A stored tensor upcast exactly to float64 (what the oracle consumes)."""
+        return getattr(self, name).to(torch.float64).numpy()
+
+
+def _draw_lengths(wl: Workload, rng: np.random.Generator) -> np.ndarray:
+    kind = wl.lengths[0]
+    if kind == "fixed":
+        vals = np.asarray(wl.lengths[1], dtype=np.int64)
+        if vals.size != wl.batch:
+            vals = np.resize(vals, wl.batch)
+    elif kind == "uniform":
+        lo, hi = wl.lengths[1], wl.lengths[2]
+        vals = rng.integers(lo, hi, size=wl.batch, endpoint=True)
+    elif kind == "lognormal":
+        median, sigma, lo, hi = wl.lengths[1:]
+        vals = np.clip(np.rint(np.exp(math.log(median) + sigma * rng.standard_normal(wl.batch))), lo, hi)
+    else:
+        raise ValueError(f"unknown length distribution {kind!r}")
+    vals = vals.astype(np.int64)
+    if (vals < wl.q_len).any():
+        raise ValueError("every sequence must hold at least q_len tokens")
+    return vals.astype(np.int32)
+
+
+def _store(x: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def make_problem(wl: Workload, seed: Optional[int] = None, *, poison: Optional[str] = "nan",
+                 seq_lens: Optional[np.ndarray] = None) -> Problem:
+    """Draw one problem.  ``seed`` defaults to the workload's base seed.
+
+    ``seq_lens`` overrides the drawn lengths (edge-case tests); the RNG still
+    draws them first so the rest of the stream does not move.
+    ``poison`` fills never-visible cache slots: "nan", "big" (+-1e4) or None.
+    """
+    seed = wl.seed_base if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = _draw_lengths(wl, rng)
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+        if lens.shape != (wl.batch,) or (lens < wl.q_len).any():
+            raise ValueError("bad seq_lens override")
+    bs = wl.block_size
+    nblk = (lens.astype(np.int64) + bs - 1) // bs
+    nb_total = int(nblk.sum())
+    mb = int(nblk.max()) if wl.batch else 0
+    perm = rng.permutation(nb_total).astype(np.int32)
+    table = np.full((wl.batch, max(mb, 1)), -1, dtype=np.int32)
+    pos = 0
+    for b in range(wl.batch):
+        table[b, : nblk[b]] = perm[pos: pos + nblk[b]]
+        pos += nblk[b]
+
+    D = wl.row_width
+    cache = _store(rng.standard_normal((nb_total, bs, D)), wl.dtype)
+    q_nope = _store(rng.standard_normal((wl.batch, wl.q_len, wl.heads, wl.d_nope)), wl.dtype)
+    q_rope = _store(rng.standard_normal((wl.batch, wl.q_len, wl.heads, wl.d_rope)), wl.dtype)
+    inv = 1.0 / math.sqrt(wl.d_c)
+    w_uk = _store(rng.standard_normal((wl.heads, wl.d_nope, wl.d_c)) * inv, wl.dtype)
+    w_uv = _store(rng.standard_normal((wl.heads, wl.d_v, wl.d_c)) * inv, wl.dtype)
+
+    if poison is not None:
+        for b in range(wl.batch):
+            tail = int(lens[b]) % bs
+            if tail:
+                blk = int(table[b, nblk[b] - 1])
+                if poison == "nan":
+                    cache[blk, tail:, :] = float("nan")
+                elif poison == "big":
+                    sign = torch.ones(bs - tail, D)
+                    sign[1::2] = -1.0
+                    cache[blk, tail:, :] = (1e4 * sign).to(cache.dtype)
+                else:
+                    raise ValueError(f"unknown poison {poison!r}")
+    return Problem(wl, seed, lens, table, cache, q_nope, q_rope, w_uk, w_uv)

@@ -1,0 +1,225 @@
+"""CPU oracle for MLA decode over a paged latent cache -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg may
+import this module.  The library never calls it and shares no code with it.
+
+Everything here is plain float64 NumPy.  The main routine takes the
+*non-absorbed* route: it up-projects every cached latent into per-head keys
+and values, then runs textbook softmax attention.  That is the formulation of
+
+  * "Deconstructing DeepSeek V4 Pro: Optimizing Multi-Head Latent Attention
+    and Auxiliary-Loss-Free Load Balancing" -- Mathematical Formulation
+    (K^C = c W_UK, V^C = c W_UV), Decoupled RoPE (K_t = [c W_UK, R(x W_KR)])
+    and the forward pass of its PyTorch module (scale 1/sqrt(d_head+d_rope),
+    softmax over the keys, weighted sum of the values);
+  * "DeepSeek-V3 MLA: Multi-Head Latent Attention Guide" -- Core Architecture
+    section 1 (k^C = W^UK c, v^C = W^UV c, W^UK in R^{(n_h d_h) x d_c}),
+    section 3 (q = [q^C; q^R], k = [k^C; k^R] with one k^R shared by all
+    heads) and its absorbed decode step, which appends the new token's latent
+    before scoring so that the current token is part of the context;
+  * "DeepSeek-V2 Multi-Head Latent Attention" knowledge note -- cache rule
+    (only c^KV and k^R are cached per token).
+
+Readings taken where the pages leave a step open: weights are stored
+W_UK[h] in R^{d_nope x d_c}, W_UV[h] in R^{d_v x d_c} (a Linear weight
+viewed per head); q_rope and the cached k_rope
+are already rotated; sequence lengths include the q_len new tokens; for
+q_len > 1, query j sees keys t <= L - q_len + j; lse is the natural-log
+log-sum-exp of the *scaled* scores; a split with no visible key has
+lse = -inf and contributes nothing to a merge.
+
+Parity status: every function below is pinned in tests/test_oracle.py
+against an independent route (absorbed algebra, a library attention routine,
+pure-Python brute force, closed forms, or figures printed on the pages).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "gather_rows",
+    "mla_decode_reference",
+    "absorb_q_reference",
+    "absorb_out_reference",
+    "lse_merge_reference",
+    "latent_attention_partial_reference",
+    "cache_elements_per_token",
+    "cache_bytes",
+]
+
+
+def gather_rows(cache: np.ndarray, block_table: np.ndarray, b: int, length: int) -> np.ndarray:
+    """Rows 0..length-1 of sequence b from a paged pool.
+
+    Token t of sequence b sits in physical block block_table[b, t // bs] at
+    slot t % bs.  Paging is not on the pages (they keep one contiguous tensor
+    per sequence); this is its plain definition.
+    """
+    bs = cache.shape[1]
+    rows = [cache[int(block_table[b, t // bs]), t % bs, :] for t in range(length)]
+    return np.stack(rows, axis=0) if rows else np.zeros((0, cache.shape[2]), dtype=cache.dtype)
+
+
+def _softmax_stats(s: np.ndarray):
+    """Textbook softmax over the last axis with max subtraction (no mask, no extras)."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=-1, keepdims=True)
+    return e / z, (m + np.log(z))[..., 0]
+
+
+def mla_decode_reference(q_nope, q_rope, cache, block_table, seq_lens, w_uk, w_uv, scale, d_c,
+                         select=None):
+    """Decode attention for every (sequence, new token, head), non-absorbed.
+
+    Shapes: q_nope [B,Lq,H,d_n], q_rope [B,Lq,H,d_r], cache [NB,bs,d_c+d_r],
+    block_table [B,MB], seq_lens [B], w_uk [H,d_n,d_c], w_uv [H,d_v,d_c].
+
+    Returns (u [B,Lq,H,d_v], o [B,Lq,H,d_c], lse [B,Lq,H]) in float64:
+      u   -- the per-head attention output sum_j p_j v_j (the primary result);
+      o   -- the latent-weighted sum sum_j p_j c_j (secondary, for intermediates);
+      lse -- log sum_j exp(score_j) of the scaled scores (secondary).
+    ``select`` (optional iterable of (b, h)) restricts the work to those
+    pairs, for spot checks at full size; every other entry is left NaN.
+    The cache may be any array type that indexes like [block, slot, :].
+    """
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    B, Lq, H, _ = q_nope.shape
+    d_v = w_uv.shape[1]
+    u = np.full((B, Lq, H, d_v), np.nan)
+    o = np.full((B, Lq, H, d_c), np.nan)
+    lse = np.full((B, Lq, H), np.nan)
+    wanted = None if select is None else {}
+    if select is not None:
+        for b, h in select:
+            wanted.setdefault(int(b), []).append(int(h))
+    for b in range(B):
+        if wanted is not None and b not in wanted:
+            continue
+        L = int(seq_lens[b])
+        if L < Lq or L > block_table.shape[1] * cache.shape[1]:
+            raise ValueError(f"sequence {b}: length {L} outside [q_len, max_blocks * block_size]")
+        rows = np.asarray(gather_rows(cache, block_table, b, L), dtype=np.float64)
+        c = rows[:, :d_c]  # cached latent c^KV for every context token
+        k_rope = rows[:, d_c:]  # cached, already-rotated shared RoPE key k^R
+        for h in (range(H) if wanted is None else wanted[b]):
+            k_content = c @ w_uk[h].T  # k^C_{t,h} = W^UK_h c_t       -> [L, d_n]
+            v = c @ w_uv[h].T  # v^C_{t,h} = W^UV_h c_t             -> [L, d_v]
+            keys = np.concatenate([k_content, k_rope], axis=1)  # k_{t,h} = [k^C; k^R]
+            for j in range(Lq):
+                last = L - Lq + j  # query j sees keys 0..last
+                q = np.concatenate([q_nope[b, j, h], q_rope[b, j, h]])  # q = [q^C; q^R]
+                s = scale * (keys[: last + 1] @ q)
+                p, lse_bjh = _softmax_stats(s[None, :])
+                p = p[0]
+                u[b, j, h] = p @ v[: last + 1]
+                o[b, j, h] = p @ c[: last + 1]
+                lse[b, j, h] = lse_bjh[0]
+    return u, o, lse
+
+
+def absorb_q_reference(q_nope, q_rope, w_uk):
+    """q_cat[b,j,h] = [ (W^UK_h)^T q^C_{b,j,h} ; q^R_{b,j,h} ].
+
+    The absorbed content query of "DeepSeek-V3 MLA: Multi-Head Latent
+    Attention Guide", Matrix Absorption Trick section 2 (Folding W^UK into
+    Query Projection), written out as a per-head matrix-vector product.
+    """
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    B, Lq, H, _ = q_nope.shape
+    d_c = w_uk.shape[2]
+    out = np.zeros((B, Lq, H, d_c + q_rope.shape[3]))
+    for h in range(H):
+        out[:, :, h, :d_c] = q_nope[:, :, h, :] @ w_uk[h]  # sum_n q[n] W[h,n,c]
+        out[:, :, h, d_c:] = q_rope[:, :, h, :]
+    return out
+
+
+def absorb_out_reference(o, w_uv):
+    """u[b,j,h] = W^UV_h o[b,j,h]: the same guide, section 3 (Absorbing W^UV)."""
+    o = np.asarray(o, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    H = o.shape[2]
+    u = np.zeros(o.shape[:3] + (w_uv.shape[1],))
+    for h in range(H):
+        u[:, :, h, :] = o[:, :, h, :] @ w_uv[h].T
+    return u
+
+
+def latent_attention_partial_reference(q_cat, rows, scale, d_c, visible):
+    """Softmax attention of absorbed queries over a subset of latent rows.
+
+    q_cat [R, D] absorbed queries, rows [T, D] latent rows, visible [R, T]
+    boolean mask.  Returns (o [R, d_c], lse [R]) with o normalised over the
+    visible rows only; a query that sees nothing gets o = 0, lse = -inf.
+    Scores are q_cat . row (the guide's score on latents: content part
+    q~ . c plus RoPE part q^R . k^R) times ``scale``.
+    """
+    q_cat = np.asarray(q_cat, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.float64)
+    R = q_cat.shape[0]
+    o = np.zeros((R, d_c))
+    lse = np.full(R, -np.inf)
+    for r in range(R):
+        idx = np.nonzero(visible[r])[0]
+        if idx.size == 0:
+            continue
+        s = scale * (rows[idx] @ q_cat[r])
+        p, l = _softmax_stats(s[None, :])
+        o[r] = p[0] @ rows[idx, :d_c]
+        lse[r] = l[0]
+    return o, lse
+
+
+def lse_merge_reference(o_parts, lse_parts):
+    """Merge normalised partial outputs over disjoint key sets.
+
+    o_parts [..., S, d], lse_parts [..., S].  Returns (o [..., d], lse [...])
+    with lse = log sum_s exp(lse_s) and o = sum_s exp(lse_s - lse) o_s.
+    Parts with lse_s = -inf hold no keys and are skipped (their o_s is never
+    read).  If every part is empty the result is o = 0, lse = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    lead = lse_parts.shape[:-1]
+    S = lse_parts.shape[-1]
+    d = o_parts.shape[-1]
+    o = np.zeros(lead + (d,))
+    lse = np.full(lead, -np.inf)
+    for idx in np.ndindex(*lead):
+        live = [s for s in range(S) if np.isfinite(lse_parts[idx + (s,)])]
+        if not live:
+            continue
+        m = max(lse_parts[idx + (s,)] for s in live)
+        z = sum(math.exp(lse_parts[idx + (s,)] - m) for s in live)
+        total = m + math.log(z)
+        lse[idx] = total
+        o[idx] = sum(math.exp(lse_parts[idx + (s,)] - total) * o_parts[idx + (s,)] for s in live)
+    return o, lse
+
+
+def cache_elements_per_token(kind: str, *, n_h=128, d_h=128, d_c=512, d_rope=64, n_kv=8) -> int:
+    """Cached elements per token per layer.
+
+    MLA keeps c^KV and k^R: d_c + d_rope.  MHA keeps K and V for every head:
+    2 n_h d_h.  GQA keeps K and V for n_kv heads: 2 n_kv d_h.
+    """
+    if kind == "mla":
+        return d_c + d_rope
+    if kind == "mha":
+        return 2 * n_h * d_h
+    if kind == "gqa":
+        return 2 * n_kv * d_h
+    raise ValueError(kind)
+
+
+def cache_bytes(kind: str, tokens: int, bytes_per_element: int, layers: int = 1, **dims) -> int:
+    """Bytes of cache for ``tokens`` tokens over ``layers`` layers."""
+    return cache_elements_per_token(kind, **dims) * tokens * bytes_per_element * layers

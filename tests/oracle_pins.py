@@ -1,0 +1,285 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` takes the oracle module as an argument so that the mutation
+tests can run the same pins against deliberately broken copies of it.  A pin
+raises AssertionError (or any exception) when the oracle is wrong.
+
+Independent routes used here:
+  * the absorbed algebra of "DeepSeek-V3 MLA: Multi-Head Latent Attention
+    Guide" (Matrix Absorption Trick, sections 2 and 3): scores on latents and
+    W^UV applied after the weighted sum -- a different computation that the
+    page shows equal to the non-absorbed one;
+  * torch.nn.functional.scaled_dot_product_attention in float64 on the CPU,
+    fed with keys and values materialised here;
+  * pure-Python scalar loops on tiny inputs;
+  * closed forms (length-1 context, zero query, constant latent rows);
+  * invariances (physical block permutation, causal reduction for q_len = 2);
+  * the log-sum-exp merge identity over a split of the keys.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+RTOL = 1e-11
+ATOL = 1e-12
+
+
+class Tiny:
+    """A tiny paged problem built from contiguous per-sequence rows.
+
+    The contiguous rows are kept, so routes below never go through the
+    oracle's own gather.
+    """
+
+    def __init__(self, seed=0, B=2, Lq=2, H=3, d_c=8, d_r=4, d_n=5, d_v=5, bs=4, lens=(5, 11),
+                 zero_query=False, const_rows=False):
+        rng = np.random.default_rng(seed)
+        self.B, self.Lq, self.H, self.d_c, self.d_r, self.d_n, self.d_v, self.bs = B, Lq, H, d_c, d_r, d_n, d_v, bs
+        self.lens = np.asarray(lens, dtype=np.int64)
+        D = d_c + d_r
+        self.rows = []
+        for L in self.lens:
+            r = rng.standard_normal((int(L), D))
+            if const_rows:
+                r[:] = r[0]
+            self.rows.append(r)
+        nblk = [int(math.ceil(L / bs)) for L in self.lens]
+        nb = sum(nblk)
+        perm = rng.permutation(nb)
+        self.table = np.full((B, max(nblk)), -1, dtype=np.int64)
+        self.cache = np.full((nb, bs, D), np.nan)
+        k = 0
+        for b in range(B):
+            for i in range(nblk[b]):
+                pb = perm[k]
+                k += 1
+                self.table[b, i] = pb
+                seg = self.rows[b][i * bs:(i + 1) * bs]
+                self.cache[pb, : seg.shape[0]] = seg
+        self.q_nope = rng.standard_normal((B, Lq, H, d_n))
+        self.q_rope = rng.standard_normal((B, Lq, H, d_r))
+        if zero_query:
+            self.q_nope[:] = 0.0
+            self.q_rope[:] = 0.0
+        self.w_uk = rng.standard_normal((H, d_n, d_c)) / math.sqrt(d_c)
+        self.w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+        self.scale = 1.0 / math.sqrt(d_n + d_r)
+
+    def run(self, orc, **kw):
+        return orc.mla_decode_reference(self.q_nope, self.q_rope, self.cache, self.table, self.lens,
+                                        self.w_uk, self.w_uv, self.scale, self.d_c, **kw)
+
+
+def _close(a, b, rtol=RTOL, atol=ATOL):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+def pin_absorbed_route(orc, seed=0):
+    """u, o, lse equal the absorbed-algebra computation on the contiguous rows."""
+    p = Tiny(seed)
+    u, o, lse = p.run(orc)
+    for b in range(p.B):
+        L = int(p.lens[b])
+        c = p.rows[b][:, : p.d_c]
+        kr = p.rows[b][:, p.d_c:]
+        for h in range(p.H):
+            for j in range(p.Lq):
+                n = L - p.Lq + j + 1
+                q_abs = np.einsum("n,nc->c", p.q_nope[b, j, h], p.w_uk[h])
+                s = (c[:n] @ q_abs + kr[:n] @ p.q_rope[b, j, h]) * p.scale
+                w = np.exp(s - s.max())
+                z = w.sum()
+                o_ref = (w / z) @ c[:n]
+                _close(o[b, j, h], o_ref)
+                _close(u[b, j, h], p.w_uv[h] @ o_ref)
+                _close(lse[b, j, h], s.max() + math.log(z))
+
+
+def pin_library_sdpa(orc, seed=1):
+    """u equals torch's float64 scaled_dot_product_attention on materialised K and V."""
+    p = Tiny(seed, H=4, lens=(9, 6))
+    u, _, _ = p.run(orc)
+    for b in range(p.B):
+        L = int(p.lens[b])
+        c = torch.from_numpy(p.rows[b][:, : p.d_c])
+        kr = torch.from_numpy(p.rows[b][:, p.d_c:])
+        wk = torch.from_numpy(p.w_uk)
+        wv = torch.from_numpy(p.w_uv)
+        K = torch.cat([torch.einsum("tc,hnc->htn", c, wk), kr.unsqueeze(0).expand(p.H, L, p.d_r)], dim=2)
+        V = torch.einsum("tc,hvc->htv", c, wv)
+        Q = torch.cat([torch.from_numpy(p.q_nope[b]), torch.from_numpy(p.q_rope[b])], dim=2).transpose(0, 1)
+        mask = torch.zeros(p.Lq, L, dtype=torch.bool)
+        for j in range(p.Lq):
+            mask[j, : L - p.Lq + j + 1] = True
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q.contiguous(), K.contiguous(), V.contiguous(), attn_mask=mask, scale=p.scale)
+        _close(u[b], ref.transpose(0, 1).numpy())
+
+
+def pin_bruteforce(orc, seed=2):
+    """u equals scalar pure-Python loops on a tiny problem."""
+    p = Tiny(seed, B=2, Lq=2, H=2, d_c=3, d_r=2, d_n=2, d_v=2, bs=2, lens=(3, 4))
+    u, _, _ = p.run(orc)
+    for b in range(p.B):
+        L = int(p.lens[b])
+        for h in range(p.H):
+            for j in range(p.Lq):
+                n = L - p.Lq + j + 1
+                scores = []
+                for t in range(n):
+                    row = [float(x) for x in p.rows[b][t]]
+                    acc = 0.0
+                    for a in range(p.d_n):
+                        k_a = sum(float(p.w_uk[h, a, cc]) * row[cc] for cc in range(p.d_c))
+                        acc += float(p.q_nope[b, j, h, a]) * k_a
+                    for r in range(p.d_r):
+                        acc += float(p.q_rope[b, j, h, r]) * row[p.d_c + r]
+                    scores.append(acc * p.scale)
+                mx = max(scores)
+                ex = [math.exp(s - mx) for s in scores]
+                z = sum(ex)
+                for vv in range(p.d_v):
+                    val = 0.0
+                    for t in range(n):
+                        v_t = sum(float(p.w_uv[h, vv, cc]) * float(p.rows[b][t][cc]) for cc in range(p.d_c))
+                        val += ex[t] / z * v_t
+                    assert abs(u[b, j, h, vv] - val) <= 1e-12 + 1e-11 * abs(val), (b, j, h, vv)
+
+
+def pin_length_one(orc, seed=3):
+    """A one-token context returns that token's value exactly (p = 1)."""
+    p = Tiny(seed, Lq=1, lens=(1, 1))
+    u, o, _ = p.run(orc)
+    for b in range(p.B):
+        c0 = p.rows[b][0, : p.d_c]
+        for h in range(p.H):
+            _close(o[b, 0, h], c0, rtol=0, atol=0)
+            _close(u[b, 0, h], p.w_uv[h] @ c0)
+
+
+def pin_zero_query(orc, seed=4):
+    """A zero query gives uniform attention: u is the mean value over visible keys."""
+    p = Tiny(seed, zero_query=True)
+    u, _, lse = p.run(orc)
+    for b in range(p.B):
+        L = int(p.lens[b])
+        for h in range(p.H):
+            v = p.rows[b][:, : p.d_c] @ p.w_uv[h].T
+            for j in range(p.Lq):
+                n = L - p.Lq + j + 1
+                _close(u[b, j, h], v[:n].mean(axis=0))
+                _close(lse[b, j, h], math.log(n))
+
+
+def pin_constant_rows(orc, seed=5):
+    """When every latent row is the same vector, softmax weights sum to one so o is that vector."""
+    p = Tiny(seed, const_rows=True)
+    _, o, _ = p.run(orc)
+    for b in range(p.B):
+        _close(o[b], np.broadcast_to(p.rows[b][0, : p.d_c], o[b].shape))
+
+
+def pin_block_permutation(orc, seed=6):
+    """Re-placing the physical blocks (and the table with them) changes nothing, bit for bit."""
+    p = Tiny(seed)
+    u1, o1, l1 = p.run(orc)
+    rng = np.random.default_rng(seed + 100)
+    nb = p.cache.shape[0]
+    perm = rng.permutation(nb)
+    cache2 = np.empty_like(p.cache)
+    cache2[perm] = p.cache
+    table2 = np.where(p.table >= 0, perm[np.maximum(p.table, 0)], -1)
+    u2, o2, l2 = orc.mla_decode_reference(p.q_nope, p.q_rope, cache2, table2, p.lens, p.w_uk, p.w_uv,
+                                          p.scale, p.d_c)
+    assert np.array_equal(u1, u2) and np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def pin_causal_reduction(orc, seed=7):
+    """For q_len = 2, query 0 equals a q_len = 1 run over the first L - 1 tokens."""
+    p = Tiny(seed, Lq=2)
+    u2, o2, l2 = p.run(orc)
+    u1, o1, l1 = orc.mla_decode_reference(p.q_nope[:, :1], p.q_rope[:, :1], p.cache, p.table, p.lens - 1,
+                                          p.w_uk, p.w_uv, p.scale, p.d_c)
+    _close(u2[:, 0], u1[:, 0])
+    _close(o2[:, 0], o1[:, 0])
+    _close(l2[:, 0], l1[:, 0])
+    # and query 1 sees one more key than query 0, so the two must differ
+    assert not np.allclose(u2[:, 0], u2[:, 1])
+
+
+def pin_merge(orc, seed=8):
+    """Splitting the keys into parts and merging (o_s, lse_s) gives the whole; empty parts count zero."""
+    p = Tiny(seed, Lq=2, lens=(7, 10))
+    _, o, lse = p.run(orc)
+    q_cat = np.concatenate([np.einsum("bjhn,hnc->bjhc", p.q_nope, p.w_uk), p.q_rope], axis=3)
+    for b in range(p.B):
+        L = int(p.lens[b])
+        bounds = [0, 2, 2, L // 2 + 1, L, L]  # includes empty parts
+        qs = q_cat[b].reshape(p.Lq * p.H, -1)
+        o_parts, l_parts = [], []
+        for s0, s1 in zip(bounds[:-1], bounds[1:]):
+            vis = np.zeros((p.Lq * p.H, s1 - s0), dtype=bool)
+            for j in range(p.Lq):
+                last = L - p.Lq + j
+                for h in range(p.H):
+                    vis[j * p.H + h] = np.arange(s0, s1) <= last
+            op, lp = orc.latent_attention_partial_reference(qs, p.rows[b][s0:s1], p.scale, p.d_c, vis)
+            o_parts.append(op)
+            l_parts.append(lp)
+        om, lm = orc.lse_merge_reference(np.stack(o_parts, axis=1), np.stack(l_parts, axis=1))
+        _close(om.reshape(p.Lq, p.H, p.d_c), o[b])
+        _close(lm.reshape(p.Lq, p.H), lse[b])
+    # all-empty merge is (0, -inf)
+    om, lm = orc.lse_merge_reference(np.full((1, 2, 3), np.nan), np.full((1, 2), -np.inf))
+    assert np.all(om == 0) and np.all(np.isneginf(lm))
+
+
+def pin_absorb_q(orc, seed=9):
+    """q_cat . [c; k^R] equals the materialised score k^C . q^C + k^R . q^R (page's associativity)."""
+    p = Tiny(seed, d_n=7)
+    q_cat = orc.absorb_q_reference(p.q_nope, p.q_rope, p.w_uk)
+    assert q_cat.shape == (p.B, p.Lq, p.H, p.d_c + p.d_r)
+    for b in range(p.B):
+        rows = p.rows[b]
+        for h in range(p.H):
+            k_c = rows[:, : p.d_c] @ p.w_uk[h].T
+            for j in range(p.Lq):
+                direct = k_c @ p.q_nope[b, j, h] + rows[:, p.d_c:] @ p.q_rope[b, j, h]
+                _close(rows @ q_cat[b, j, h], direct)
+
+
+def pin_absorb_out(orc, seed=10):
+    """W^UV applied to o equals the weighted sum of materialised values (u from the non-absorbed route)."""
+    p = Tiny(seed, d_v=6)
+    u, o, _ = p.run(orc)
+    _close(orc.absorb_out_reference(o, p.w_uv), u)
+
+
+def pin_select(orc, seed=11):
+    """Restricting to chosen (b, h) pairs reproduces exactly those entries of the full run."""
+    p = Tiny(seed)
+    u, o, lse = p.run(orc)
+    sel = [(1, 2), (0, 0)]
+    us, os_, ls = p.run(orc, select=sel)
+    for b, h in sel:
+        assert np.array_equal(us[b, :, h], u[b, :, h]) and np.array_equal(ls[b, :, h], lse[b, :, h])
+    assert np.isnan(us[0, :, 1]).all()
+
+
+ALL_PINS = [
+    pin_absorbed_route,
+    pin_library_sdpa,
+    pin_bruteforce,
+    pin_length_one,
+    pin_zero_query,
+    pin_constant_rows,
+    pin_block_permutation,
+    pin_causal_reduction,
+    pin_merge,
+    pin_absorb_q,
+    pin_absorb_out,
+    pin_select,
+]
