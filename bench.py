@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for libmla on one MI355X.
+
+A step is one pass of the whole hot path over one batch: plan, absorb_q,
+split-KV attention, log-sum-exp combine, absorb_out, for every sequence of
+the workload.  Inputs are seeded synthetic tensors already resident in HBM.
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "batch64_1k8k_bf16"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+KERNEL_SOURCES = ["mla_latent_kv_14_amd/csrc/decode_mfma.hip", "mla_latent_kv_14_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_batch64_1k8k_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(prob):
+    """Bytes and flops the attention kernel must move / do for one launch.
+
+    Bytes: every visible cache row once (d_c + d_rope elements), the absorbed
+    queries, the block-table entries used, the sequence lengths, and the
+    latent output o (float32).  Split partials are implementation overhead
+    and not counted.  Flops: 2 * (d_c + d_rope) for the score plus 2 * d_c
+    for the weighted sum, per visible (query row, token) pair.
+    """
+    wl = prob.wl
+    esz = 4 if wl.dtype == "f32" else 2
+    D = wl.d_c + wl.d_rope
+    L = prob.seq_lens.astype(np.int64)
+    rows_bytes = int(L.sum()) * D * esz
+    q_bytes = wl.batch * wl.q_len * wl.heads * D * esz
+    table_bytes = int(((L + wl.block_size - 1) // wl.block_size).sum()) * 4 + wl.batch * 4
+    o_bytes = wl.batch * wl.q_len * wl.heads * wl.d_c * 4
+    visible = sum(int((L - wl.q_len + j + 1).sum()) for j in range(wl.q_len))
+    flops = 2 * wl.heads * visible * (D + wl.d_c)
+    return rows_bytes + q_bytes + table_bytes + o_bytes, flops
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        p = os.path.join(ROOT, rel)
+        if os.path.exists(p):
+            with open(p, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per attention launch from committed rocprofv3 counters, if they match this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(prob, budget_s=15.0, max_s=30.0):
+    """Time the float64 oracle on the first sequences of the same workload."""
+    from oracle import mla_oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    wl = prob.wl
+    cache = prob.cache.float().numpy() if wl.dtype == "bf16" else prob.cache.numpy()
+    qn, qr = prob.f64("q_nope"), prob.f64("q_rope")
+    wuk, wuv = prob.f64("w_uk"), prob.f64("w_uv")
+    done, tokens_ctx = 0, 0
+    t0 = time.perf_counter()
+    for b in range(wl.batch):
+        sel = [(b, h) for h in range(wl.heads)]
+        orc.mla_decode_reference(qn, qr, cache, prob.block_table, prob.seq_lens, wuk, wuv, prob.scale, wl.d_c,
+                                 select=sel)
+        done += 1
+        tokens_ctx += int(prob.seq_lens[b])
+        el = time.perf_counter() - t0
+        if el >= budget_s or el >= max_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": done * wl.q_len / el,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} of {wl.batch} sequences ({tokens_ctx} context tokens), all {wl.heads} heads, "
+                   f"float64 non-absorbed route, {el:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: libmla has no multi-GPU path (whole sequences would shard "
+              "across GPUs with no exchange). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mla_latent_kv_14_amd.inputs import make_problem, workload
+    from mla_latent_kv_14_amd.runner import DecodeRunner
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    wl = workload(args.workload)
+    log(f"bench: generating {wl.name} ...")
+    prob = make_problem(wl, args.seed)
+    r = DecodeRunner(prob, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    log(f"bench: B={wl.batch} H={wl.heads} Lq={wl.q_len} tokens={prob.total_tokens} splits={r.num_splits}")
+
+    calls = [("plan", r.plan), ("absorb_q", r.absorb_q), ("decode", r.decode_planned), ("combine", r.combine),
+             ("absorb_out", r.absorb_out)]
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    K = args.steps
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+          for n, _ in calls}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        for n, fn in calls:
+            ev[n][i][0].record(stream)
+            fn()
+            ev[n][i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n, _ in calls}
+    log(f"bench: {ms_step * 1e3:.1f} us/step; per call (us): " +
+        ", ".join(f"{n}={v:.1f}" for n, v in per_call_us.items()))
+
+    alg_bytes, flops = algorithmic_work(prob)
+    dec_s = per_call_us["decode"] * 1e-6
+    achieved_gbs = alg_bytes / dec_s / 1e9
+    achieved_tflops = flops / dec_s / 1e12
+    tokens = wl.batch * wl.q_len
+    traffic = measured_traffic(wl.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(prob)
+
+    rec = {
+        "metric": "MLA decode tokens/s + TFLOP/s & HBM GB/s vs roofline, B=64 H=128 ctx 1K-8K",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_len": wl.q_len, "d_c": wl.d_c,
+                   "d_rope": wl.d_rope, "d_nope": wl.d_nope, "d_v": wl.d_v, "block_size": wl.block_size,
+                   "context_tokens": prob.total_tokens, "lengths": " ".join(str(x) for x in wl.lengths),
+                   "num_splits": r.num_splits},
+        "roofline": {"kernel": "mla_decode attention", "bound": "hbm", "achieved": achieved_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
+                     "mfma_tflops": achieved_tflops, "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "per_call_us": per_call_us,
+        "step_tflops": flops / (ms_step * 1e-3) / 1e12,
+        "step_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * libmla -- absorbed Multi-Head Latent Attention (MLA) decode over a paged
+ * latent cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For each sequence b, new token j < q_len and head h the
+ * library evaluates decode attention in the "absorbed" form of
+ * "DeepSeek-V3 MLA: Multi-Head Latent Attention Guide" (section Inference
+ * Optimization: The Matrix Absorption Trick):
+ *
+ *   q~      = (W^UK_h)^T q^C                        (section 2, Folding W^UK)
+ *   s_t     = scale * ( q~ . c_t  +  q^R . k^R_t )  (section 2, score on latents)
+ *   p       = softmax_t(s) over the visible t       (textbook softmax)
+ *   o       = sum_t p_t c_t                         (section 3, o_{t,i})
+ *   u       = W^UV_h o                              (section 3, u_{t,i})
+ *
+ * so the per-head keys W^UK c_t and values W^UV c_t are never formed.  The
+ * cache holds, per token, only the joint latent c^KV (d_c) and the decoupled,
+ * already-rotated RoPE key k^R (d_rope) shared by all heads ("DeepSeek-V2
+ * Multi-Head Latent Attention" knowledge note, cache rule and Decoupled RoPE).
+ *
+ * Pipeline (four calls, all asynchronous on the caller's stream):
+ *   mla_absorb_q   q_nope, q_rope, W_UK        -> q_cat  [B,Lq,H,d_c+d_rope]
+ *   mla_decode     q_cat, paged cache          -> per-split (o_s, lse_s)
+ *   mla_combine    (o_s, lse_s)                -> o [B,Lq,H,d_c], lse [B,Lq,H]
+ *   mla_absorb_out o, W_UV                     -> u [B,Lq,H,d_v]
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to row-major, contiguous arrays with
+ *     the shapes given per call; every base pointer must be 16-byte aligned.
+ *   - "storage type" is dims->dtype: MLA_F32 (float) or MLA_BF16 (bfloat16,
+ *     raw 16-bit patterns).  Accumulation is always float32.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     retains a pointer, and keeps no state besides a per-device properties
+ *     cache filled once.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     call only enqueues work; it never synchronises.  Inputs must stay valid
+ *     until the stream reaches the call; outputs are ready once it has.
+ *   - The return value is an mla_status.  Arguments are validated on the host
+ *     before anything is enqueued; on failure nothing is launched or written.
+ *     A launch failure returns MLA_ERR_HIP.  Values that live only on the
+ *     device (seq_lens, block ids) cannot be checked on the host: a sequence
+ *     length outside [q_len, max_blocks_per_seq * block_size] or a block id
+ *     outside [0, num_blocks) is undefined behaviour.
+ *   - No exception crosses this interface.
+ */
+#ifndef LIBMLA_MLA_H
+#define LIBMLA_MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, misaligned pointer, bad split count */
+  MLA_ERR_UNSUPPORTED = -2, /* valid but not implemented: dtype, widths or q_len outside the supported set */
+  MLA_ERR_HIP = -4          /* the HIP runtime reported an error (launch or device query) */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Problem dimensions.  Widths follow DeepSeek-V2/V3 notation: d_c is the KV
+ * latent width (512), d_rope the decoupled RoPE width (64), d_nope the per-head
+ * content query/key width d_h (128), d_v the per-head value width (128). */
+typedef struct {
+  int32_t batch;              /* B: number of sequences */
+  int32_t q_len;              /* Lq: new tokens per sequence, 1 or 2 */
+  int32_t num_heads;          /* H */
+  int32_t d_c;                /* latent width, multiple of 16, <= 1024 */
+  int32_t d_rope;             /* RoPE key width, multiple of 8, d_c + d_rope <= 1088 */
+  int32_t d_nope;             /* content query width, <= 1024 */
+  int32_t d_v;                /* value width, <= 1024 */
+  int32_t block_size;         /* tokens per physical cache block */
+  int32_t max_blocks_per_seq; /* MB: row length of block_table */
+  int32_t num_blocks;         /* NB: blocks in the cache pool */
+  int32_t dtype;              /* mla_dtype: storage type of q, cache and weights */
+} mla_dims;
+
+/* Absorb W^UK into the query ("DeepSeek-V3 MLA: Multi-Head Latent Attention
+ * Guide", Matrix Absorption Trick section 2, Folding W^UK into Query
+ * Projection):
+ *   q_cat[b,j,h, 0:d_c]        = sum_n q_nope[b,j,h,n] * w_uk[h,n,:]
+ *   q_cat[b,j,h, d_c:d_c+d_r]  = q_rope[b,j,h,:]
+ * q_nope [B,Lq,H,d_nope], q_rope [B,Lq,H,d_rope], w_uk [H,d_nope,d_c] (a
+ * Linear weight of shape (H*d_nope) x d_c viewed per head), q_cat
+ * [B,Lq,H,d_c+d_rope]; all in the storage type (q~ is rounded once to it). */
+int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
+                 void* q_cat, void* stream);
+
+/* Number of splits S that mla_decode needs so that the device's full grid
+ * shares the work evenly, given the longest sequence and the total token
+ * count (host-side values the caller knows).  Result in [1, 4096].  Passing a
+ * smaller S to mla_decode is allowed: the library then gives each workgroup a
+ * longer token range and launches fewer of them. */
+int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total_tokens,
+                          int32_t* num_splits);
+
+/* Bytes of device workspace mla_decode needs (the work schedule it computes
+ * on the device: a few words plus one int32 per sequence). */
+int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t* bytes);
+
+/* Split-KV attention over the paged latent cache (the guide's section 4,
+ * End-to-End Latent Attention Computation: scores and latent-weighted sums
+ * in one fused pass over rows loaded once into on-chip memory).
+ *   q_cat       [B,Lq,H,d_c+d_rope]   storage type, from mla_absorb_q
+ *   kv_cache    [NB,block_size,d_c+d_rope] storage type; row = [c^KV | k^R]
+ *   block_table [B,MB] int32: token t of sequence b is at
+ *               kv_cache[block_table[b, t / block_size], t % block_size, :]
+ *   seq_lens    [B] int32: tokens of sequence b INCLUDING its q_len new
+ *               ones; query j sees tokens t <= seq_lens[b] - q_len + j
+ *   softmax_scale  multiplies every score (1/sqrt(d_nope + d_rope) for MLA);
+ *               must be finite and > 0
+ *   num_splits  S >= 1, the split dimension of the two outputs
+ *   workspace   device scratch of at least mla_decode_workspace_bytes(),
+ *               16-byte aligned; overwritten by every call, so calls sharing
+ *               one workspace must be ordered on one stream
+ *   o_partial   [B,Lq,H,S,d_c] float32: o_s = sum_{t in split} p_t c_t with p
+ *               normalised within the split
+ *   lse_partial [B,Lq,H,S] float32: natural-log log-sum-exp of the split's
+ *               scaled scores; -inf marks an unused or empty split, whose
+ *               o_partial entry is left unwritten.
+ * Equivalent to mla_decode_plan followed by mla_decode_planned (two kernels:
+ * a one-workgroup planner that turns seq_lens into a token-balanced schedule
+ * in the workspace, then the attention kernel).  Each sequence's tokens are
+ * divided into at most S contiguous ranges.  Unused cache slots may hold
+ * anything (NaN included): they never reach a result.  A length outside
+ * [0, MB * block_size] is clamped into it for memory safety (the result for
+ * that sequence is then meaningless). */
+int mla_decode(const mla_dims* dims, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+               const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream);
+
+/* First half of mla_decode: enqueue only the planner, which writes the work
+ * schedule for seq_lens [B] int32 (device) and num_splits into the workspace.
+ * One plan serves every later mla_decode_planned call with the same dims,
+ * lengths and num_splits, e.g. all layers of one decode step. */
+int mla_decode_plan(const mla_dims* dims, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Second half of mla_decode: enqueue only the attention kernel, reading the
+ * schedule (and the lengths) that mla_decode_plan left in the workspace.
+ * Arguments as for mla_decode; num_splits must equal the planned value. */
+int mla_decode_planned(const mla_dims* dims, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                       float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                       float* o_partial, float* lse_partial, void* stream);
+
+/* Log-sum-exp merge of the splits (exact rewrite of one softmax over the
+ * union of the splits' keys):
+ *   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s
+ * skipping splits with lse_s = -inf.  o_partial/lse_partial as written by
+ * mla_decode; o_latent [B,Lq,H,d_c] float32; lse [B,Lq,H] float32 or NULL. */
+int mla_combine(const mla_dims* dims, int32_t num_splits, const float* o_partial, const float* lse_partial,
+                float* o_latent, float* lse, void* stream);
+
+/* Apply W^UV after the latent-weighted sum ("DeepSeek-V3 MLA: Multi-Head
+ * Latent Attention Guide", Matrix Absorption Trick section 3, Absorbing
+ * W^UV):  u[b,j,h,v] = sum_c w_uv[h,v,c] * o_latent[b,j,h,c].
+ * o_latent [B,Lq,H,d_c] float32, w_uv [H,d_v,d_c] storage type, out
+ * [B,Lq,H,d_v] storage type. */
+int mla_absorb_out(const mla_dims* dims, const float* o_latent, const void* w_uv, void* out, void* stream);
+
+/* Static description of a status code. */
+const char* mla_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMLA_MLA_H */

@@ -1,0 +1,204 @@
+"""ctypes binding of libmla.so: the same entry points, taking torch tensors.
+
+Argument marshalling only: each function checks that tensors are contiguous
+device tensors of the expected dtype and size (a host pointer handed to a GPU
+kernel would fault the device), then calls the C function of the same name on
+the current (or given) HIP stream.  Every computation runs in libmla's HIP
+kernels; there is no fallback of any kind.  A missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, -1, -2, -4
+MLA_F32, MLA_BF16 = 0, 1
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+class mla_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "q_len", "num_heads", "d_c", "d_rope", "d_nope", "d_v", "block_size", "max_blocks_per_seq",
+        "num_blocks", "dtype")]
+
+    def __repr__(self):
+        return "mla_dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_latent_kv_14_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(mla_dims)
+    sig = {
+        "mla_absorb_q": [D, P, P, P, P, P],
+        "mla_decode_num_splits": [D, I32, I64, ctypes.POINTER(I32)],
+        "mla_decode_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
+        "mla_decode": [D, P, P, P, P, F32, I32, P, SZ, P, P, P],
+        "mla_decode_plan": [D, P, I32, P, SZ, P],
+        "mla_decode_planned": [D, P, P, P, F32, I32, P, SZ, P, P, P],
+        "mla_combine": [D, I32, P, P, P, P, P],
+        "mla_absorb_out": [D, P, P, P, P],
+        "mla_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.mla_status_str.argtypes = [ctypes.c_int]
+    lib.mla_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/mla.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_str(status: int) -> str:
+    return load().mla_status_str(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MLA_OK:
+        raise MLAError(fn, status, status_str(status))
+
+
+def make_dims(batch, q_len, num_heads, d_c, d_rope, d_nope, d_v, block_size, max_blocks_per_seq, num_blocks,
+              dtype) -> mla_dims:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: MLA_F32, torch.bfloat16: MLA_BF16}[dtype]
+    return mla_dims(batch, q_len, num_heads, d_c, d_rope, d_nope, d_v, block_size, max_blocks_per_seq, num_blocks,
+                    dtype)
+
+
+def _storage_dtype(dims: mla_dims) -> torch.dtype:
+    return torch.float32 if dims.dtype == MLA_F32 else torch.bfloat16
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, numel: int):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def mla_absorb_q(dims, q_nope, q_rope, w_uk, q_cat, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    _check("mla_absorb_q", load().mla_absorb_q(
+        ctypes.byref(d), _ptr(q_nope, "q_nope", st, rows * d.d_nope), _ptr(q_rope, "q_rope", st, rows * d.d_rope),
+        _ptr(w_uk, "w_uk", st, d.num_heads * d.d_nope * d.d_c),
+        _ptr(q_cat, "q_cat", st, rows * (d.d_c + d.d_rope)), _stream(stream)))
+
+
+def mla_decode_num_splits(dims, max_seq_len: int, total_tokens: int) -> int:
+    out = ctypes.c_int32(0)
+    _check("mla_decode_num_splits", load().mla_decode_num_splits(ctypes.byref(dims), int(max_seq_len),
+                                                                 int(total_tokens), ctypes.byref(out)))
+    return out.value
+
+
+def mla_decode_workspace_bytes(dims, num_splits: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_decode_workspace_bytes",
+           load().mla_decode_workspace_bytes(ctypes.byref(dims), int(num_splits), ctypes.byref(out)))
+    return out.value
+
+
+def mla_decode(dims, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, workspace, o_partial,
+               lse_partial, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    D = d.d_c + d.d_rope
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_decode", load().mla_decode(
+        ctypes.byref(d), _ptr(q_cat, "q_cat", st, rows * D),
+        _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch), float(softmax_scale), int(num_splits),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
+
+
+def mla_decode_plan(dims, seq_lens, num_splits, workspace, stream=None):
+    d = dims
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_decode_plan", load().mla_decode_plan(
+        ctypes.byref(d), _ptr(seq_lens, "seq_lens", torch.int32, d.batch), int(num_splits),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_decode_planned(dims, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, o_partial,
+                       lse_partial, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    D = d.d_c + d.d_rope
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_decode_planned", load().mla_decode_planned(
+        ctypes.byref(d), _ptr(q_cat, "q_cat", st, rows * D),
+        _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq), float(softmax_scale),
+        int(num_splits), ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
+
+
+def mla_combine(dims, num_splits, o_partial, lse_partial, o_latent, lse=None, stream=None):
+    d = dims
+    rows = d.batch * d.q_len * d.num_heads
+    _check("mla_combine", load().mla_combine(
+        ctypes.byref(d), int(num_splits), _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits),
+        _ptr(o_latent, "o_latent", torch.float32, rows * d.d_c),
+        _ptr(lse, "lse", torch.float32, rows) if lse is not None else None, _stream(stream)))
+
+
+def mla_absorb_out(dims, o_latent, w_uv, out, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    _check("mla_absorb_out", load().mla_absorb_out(
+        ctypes.byref(d), _ptr(o_latent, "o_latent", torch.float32, rows * d.d_c),
+        _ptr(w_uv, "w_uv", st, d.num_heads * d.d_v * d.d_c), _ptr(out, "out", st, rows * d.d_v), _stream(stream)))

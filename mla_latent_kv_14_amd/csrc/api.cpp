@@ -1,0 +1,249 @@
+// C-ABI front end of libmla: host-side validation, kernel selection, launches.
+//
+// Every entry point validates its arguments completely before the first HIP
+// call, so an invalid call enqueues nothing and touches no buffer.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "common.h"
+#include "internal.h"
+#include "mla.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kMaxSplits = 4096;
+constexpr int kMaxBatch = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+int check_dims(const mla_dims* d) {
+  if (d == nullptr) return MLA_ERR_INVALID_ARG;
+  if (d->batch <= 0 || d->q_len <= 0 || d->num_heads <= 0 || d->d_c <= 0 || d->d_rope < 0 || d->d_nope <= 0 ||
+      d->d_v <= 0 || d->block_size <= 0 || d->max_blocks_per_seq <= 0 || d->num_blocks <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (d->batch > kMaxBatch) return MLA_ERR_UNSUPPORTED;
+  if (d->q_len > 8) return MLA_ERR_UNSUPPORTED;
+  if (d->d_c % 16 != 0 || d->d_c > 1024) return MLA_ERR_UNSUPPORTED;
+  if (d->d_rope % 8 != 0 || d->d_c + d->d_rope > 1088) return MLA_ERR_UNSUPPORTED;
+  if (d->d_nope > 1024 || d->d_v > 1024) return MLA_ERR_UNSUPPORTED;
+  if (d->num_heads > 4096) return MLA_ERR_UNSUPPORTED;
+  // every index the kernels form must fit comfortably in 31 bits per dimension product
+  const int64_t max_len = (int64_t)d->max_blocks_per_seq * d->block_size;
+  if (max_len > (int64_t)1 << 30) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Per-device compute-unit count, queried once per device.
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static int cache[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return MLA_ERR_HIP;
+    cache[dev] = n;
+  }
+  *cus = cache[dev];
+  return MLA_OK;
+}
+
+// Which decode kernel serves these dimensions.  MLA_DECODE_KERNEL=generic forces
+// the portable kernel (both are HIP; this is for cross-checking).
+enum class DecodeKind { Generic };
+
+DecodeKind pick_decode(const mla_dims& d) {
+  (void)d;
+  return DecodeKind::Generic;
+}
+
+struct DecodeShape {
+  int grid;       // workgroups launched along the split axis
+  int min_chunk;  // smallest token range (in 64-token tiles) worth one workgroup
+};
+
+int decode_shape(const mla_dims& d, DecodeShape* out) {
+  int cus = 0;
+  int st = device_cus(&cus);
+  if (st != MLA_OK) return st;
+  switch (pick_decode(d)) {
+    case DecodeKind::Generic: {
+      const int R = d.q_len * d.num_heads;
+      const int row_groups = (R + mla::decode_generic_rows_per_group() - 1) / mla::decode_generic_rows_per_group();
+      // about eight resident workgroups per CU over all row groups
+      int g = (cus * 8 + row_groups - 1) / row_groups;
+      out->grid = g < 1 ? 1 : g;
+      out->min_chunk = 1;
+      return MLA_OK;
+    }
+  }
+  return MLA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(int s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dimensions or dtype";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int mla_version(void) { return 100; }
+
+int mla_absorb_q(const mla_dims* d, const void* q_nope, const void* q_rope, const void* w_uk, void* q_cat,
+                 void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(q_nope) || !ptr_ok(w_uk) || !ptr_ok(q_cat) || (d->d_rope > 0 && !ptr_ok(q_rope)))
+    return MLA_ERR_INVALID_ARG;
+  return to_status(mla::launch_absorb_q_generic(*d, q_nope, q_rope, w_uk, q_cat, (hipStream_t)stream));
+}
+
+int mla_decode_workspace_bytes(const mla_dims* d, int32_t num_splits, size_t* bytes) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr || num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  const size_t b = mla::workspace_words(d->batch) * sizeof(int32_t);
+  *bytes = (b + 255) / 256 * 256;
+  return MLA_OK;
+}
+
+int mla_decode_num_splits(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (num_splits == nullptr || max_seq_len <= 0 || total_tokens < max_seq_len) return MLA_ERR_INVALID_ARG;
+  DecodeShape sh;
+  st = decode_shape(*d, &sh);
+  if (st != MLA_OK) return st;
+  const int64_t tile = 64;
+  const int64_t total_tiles = (total_tokens + tile - 1) / tile;  // lower bound of the planner's sum, so S is never too small
+  int64_t chunk = (total_tiles + sh.grid - 1) / sh.grid;
+  if (chunk < sh.min_chunk) chunk = sh.min_chunk;
+  const int64_t maxn = (max_seq_len + tile - 1) / tile;
+  int64_t s = (maxn <= 1) ? 1 : (maxn - 1 + chunk - 1) / chunk + 1;
+  if (s < 2 && maxn > 1) s = 2;
+  if (s > kMaxSplits) s = kMaxSplits;
+  *num_splits = (int32_t)s;
+  return MLA_OK;
+}
+
+namespace {
+
+int check_decode_common(const mla_dims* d, int32_t num_splits, const void* workspace, size_t workspace_bytes) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(workspace)) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  size_t need = 0;
+  mla_decode_workspace_bytes(d, num_splits, &need);
+  if (workspace_bytes < need) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
+
+int check_attention_args(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                         float softmax_scale, float* o_partial, float* lse_partial) {
+  if (!ptr_ok(q_cat) || !ptr_ok(kv_cache) || !ptr_ok(block_table) || !ptr_ok(o_partial) || !ptr_ok(lse_partial))
+    return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale || softmax_scale == INFINITY)
+    return MLA_ERR_INVALID_ARG;
+  (void)d;
+  return MLA_OK;
+}
+
+hipError_t enqueue_plan(const mla_dims& d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                        const DecodeShape& sh, hipStream_t s) {
+  return mla::launch_plan(d, seq_lens, num_splits, sh.grid, sh.min_chunk, static_cast<int32_t*>(workspace), s);
+}
+
+hipError_t enqueue_attention(const mla_dims& d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                             float softmax_scale, int32_t num_splits, const void* workspace, const DecodeShape& sh,
+                             float* o_partial, float* lse_partial, hipStream_t s) {
+  const int32_t* ws = static_cast<const int32_t*>(workspace);
+  switch (pick_decode(d)) {
+    case DecodeKind::Generic:
+      return mla::launch_decode_generic(d, q_cat, kv_cache, block_table, ws, softmax_scale, num_splits, sh.grid,
+                                        o_partial, lse_partial, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int mla_decode_plan(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(seq_lens)) return MLA_ERR_INVALID_ARG;
+  DecodeShape sh;
+  st = decode_shape(*d, &sh);
+  if (st != MLA_OK) return st;
+  return to_status(enqueue_plan(*d, seq_lens, num_splits, workspace, sh, (hipStream_t)stream));
+}
+
+int mla_decode_planned(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                       float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                       float* o_partial, float* lse_partial, void* stream) {
+  int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial);
+  if (st != MLA_OK) return st;
+  DecodeShape sh;
+  st = decode_shape(*d, &sh);
+  if (st != MLA_OK) return st;
+  return to_status(enqueue_attention(*d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, sh,
+                                     o_partial, lse_partial, (hipStream_t)stream));
+}
+
+int mla_decode(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+               const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+  int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(seq_lens)) return MLA_ERR_INVALID_ARG;
+  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial);
+  if (st != MLA_OK) return st;
+  DecodeShape sh;
+  st = decode_shape(*d, &sh);
+  if (st != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = enqueue_plan(*d, seq_lens, num_splits, workspace, sh, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return to_status(enqueue_attention(*d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, sh,
+                                     o_partial, lse_partial, s));
+}
+
+int mla_combine(const mla_dims* d, int32_t num_splits, const float* o_partial, const float* lse_partial,
+                float* o_latent, float* lse, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(o_partial) || !ptr_ok(lse_partial) || !ptr_ok(o_latent) || (lse != nullptr && !aligned16(lse)))
+    return MLA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  return to_status(mla::launch_combine(*d, num_splits, o_partial, lse_partial, o_latent, lse, (hipStream_t)stream));
+}
+
+int mla_absorb_out(const mla_dims* d, const float* o_latent, const void* w_uv, void* out, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(o_latent) || !ptr_ok(w_uv) || !ptr_ok(out)) return MLA_ERR_INVALID_ARG;
+  return to_status(mla::launch_absorb_out_generic(*d, o_latent, w_uv, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+// Shared definitions for the libmla HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// Planning granularity: the schedule hands out whole 64-token tiles of a
+// sequence.  A workgroup's token range therefore starts at a multiple of 64
+// within its sequence and ends at a multiple of 64 or at the sequence end.
+constexpr int kPlanTile = 64;
+
+// Workspace layout written by the planner (int32 words):
+//   [0] chunk   tiles per workgroup (>= 1), or 0 in one-sequence-per-workgroup mode
+//   [1] groups  number of workgroups that have work (<= launched grid)
+//   [2] total   total tiles over all sequences
+//   [3] maxn    tiles of the longest sequence
+//   [4] splits  S as passed by the caller
+//   [5] error   0, or 1 + index of the first sequence whose length was out of range
+//   [6] batch   B
+//   [7] reserved
+//   [8 .. 8+B]        cu: exclusive prefix sum of tiles per sequence (B + 1 words)
+//   [9+B .. 9+2B)     len: per-sequence length, clamped to [0, MB * block_size]
+constexpr int kWsHeader = 8;
+inline size_t workspace_words(int batch) { return (size_t)kWsHeader + 2 * (size_t)batch + 1; }
+
+struct DecodeArgs {
+  const void* q_cat;
+  const void* cache;
+  const int32_t* block_table;
+  const int32_t* ws;  // planner output
+  float* o_part;
+  float* lse_part;
+  float scale;
+  int32_t B, Lq, H, d_c, d_rope, block_size, max_blocks, num_blocks, splits;
+};
+
+// ---- float <-> storage conversions -------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Storage;
+template <> struct Storage<float> {
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Storage<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  __device__ __forceinline__ static void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+// ---- wave64 reductions ---------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// ---- schedule lookups shared by every decode kernel ----------------------------------
+
+// Largest b in [0, B) with cu[b] <= tile (cu is non-decreasing, cu[0] = 0).
+__device__ __forceinline__ int find_sequence(const int32_t* cu, int B, int tile) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One contiguous piece of one sequence handled by one workgroup.
+struct Segment {
+  int b;          // sequence
+  int tok_begin;  // first token (inclusive)
+  int tok_end;    // last token + 1 (clamped to the sequence length)
+  int split;      // index of this piece among the sequence's pieces
+  int nsplits;    // pieces the sequence is divided into
+};
+
+// Iterates the segments of workgroup w under the planner's schedule.
+struct SegmentWalker {
+  const int32_t* ws;
+  int B, w, chunk, groups, total;
+  int b;         // current sequence
+  int t_begin;   // workgroup's first tile, t_end its end (chunked mode)
+  int t_end;
+
+  __device__ __forceinline__ void init(const int32_t* ws_, int w_) {
+    ws = ws_;
+    w = w_;
+    chunk = ws[0];
+    groups = ws[1];
+    total = ws[2];
+    B = ws[6];
+    if (chunk > 0) {
+      t_begin = w * chunk;
+      t_end = min(t_begin + chunk, total);
+      b = (t_begin < total) ? find_sequence(ws + kWsHeader, B, t_begin) : B;
+    } else {
+      b = w;  // one whole sequence per step, stride = groups
+    }
+  }
+
+  // Returns false when the workgroup has no more work.
+  __device__ __forceinline__ bool next(Segment& s) {
+    const int32_t* cu = ws + kWsHeader;
+    const int32_t* len = ws + kWsHeader + B + 1;
+    if (chunk > 0) {
+      // skip zero-tile sequences
+      while (b < B && cu[b + 1] <= t_begin) ++b;
+      if (b >= B || t_begin >= t_end || cu[b] >= t_end) return false;
+      const int c0 = cu[b], c1 = cu[b + 1];
+      const int lo = max(t_begin, c0), hi = min(t_end, c1);
+      s.b = b;
+      s.tok_begin = (lo - c0) * kPlanTile;
+      s.tok_end = min((hi - c0) * kPlanTile, len[b]);
+      const int first = c0 / chunk;
+      s.split = w - first;
+      s.nsplits = (c1 - 1) / chunk - first + 1;
+      t_begin = hi;
+      ++b;
+      return true;
+    }
+    if (b >= B) return false;
+    s.b = b;
+    s.tok_begin = 0;
+    s.tok_end = len[b];
+    s.split = 0;
+    s.nsplits = 1;
+    b += groups;
+    return true;
+  }
+};
+
+// A sequence with no tokens is visited by no workgroup; workgroup 0 marks all
+// of its splits empty.  `row` is the query row (j * H + h) this lane group owns.
+__device__ __forceinline__ void mark_empty_sequences(const DecodeArgs& a, int row, int lane, int lanes) {
+  const int32_t* len = a.ws + kWsHeader + a.B + 1;
+  const int R = a.Lq * a.H;
+  for (int b = 0; b < a.B; ++b) {
+    if (len[b] != 0) continue;
+    float* lp = a.lse_part + ((size_t)b * R + row) * a.splits;
+    for (int s = lane; s < a.splits; s += lanes) lp[s] = -INFINITY;
+  }
+}
+
+}  // namespace mla

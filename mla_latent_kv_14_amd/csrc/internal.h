@@ -1,0 +1,27 @@
+// Launchers shared between the C-ABI front end (api.cpp) and the kernel files.
+// Every launcher assumes its arguments were validated by the front end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// planner (plan.hip)
+hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk,
+                       int32_t* ws, hipStream_t stream);
+
+// portable kernels for any supported shape (generic.hip)
+hipError_t launch_absorb_q_generic(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
+                                   void* q_cat, hipStream_t stream);
+hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
+                                 const int32_t* ws, float scale, int splits, int grid, float* o_part,
+                                 float* lse_part, hipStream_t stream);
+int decode_generic_rows_per_group();
+hipError_t launch_combine(const mla_dims& d, int splits, const float* o_part, const float* lse_part, float* o,
+                          float* lse, hipStream_t stream);
+hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const void* w_uv, void* out,
+                                     hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,74 @@
+"""Device-resident buffers for one decode problem plus the four-call step.
+
+Allocation and upload use torch (device memory only); every step of the
+computation is a libmla call.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as libmla
+from .inputs import Problem
+
+
+class DecodeRunner:
+    """Holds a problem's inputs, workspace and outputs on one device."""
+
+    def __init__(self, prob: Problem, device="cuda", num_splits: Optional[int] = None):
+        self.prob = prob
+        wl = prob.wl
+        self.device = torch.device(device)
+        self.dims = libmla.make_dims(wl.batch, wl.q_len, wl.heads, wl.d_c, wl.d_rope, wl.d_nope, wl.d_v,
+                                     wl.block_size, prob.max_blocks, prob.num_blocks,
+                                     torch.float32 if wl.dtype == "f32" else torch.bfloat16)
+        dev = self.device
+        self.cache = prob.cache.to(dev)
+        self.q_nope = prob.q_nope.to(dev)
+        self.q_rope = prob.q_rope.to(dev)
+        self.w_uk = prob.w_uk.to(dev)
+        self.w_uv = prob.w_uv.to(dev)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(prob.block_table)).to(dev)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(prob.seq_lens)).to(dev)
+        if num_splits is None:
+            num_splits = libmla.mla_decode_num_splits(self.dims, int(prob.seq_lens.max()), prob.total_tokens)
+        self.num_splits = int(num_splits)
+        B, Lq, H = wl.batch, wl.q_len, wl.heads
+        st = self.cache.dtype
+        self.q_cat = torch.empty((B, Lq, H, wl.d_c + wl.d_rope), dtype=st, device=dev)
+        ws_bytes = libmla.mla_decode_workspace_bytes(self.dims, self.num_splits)
+        self.workspace = torch.empty(ws_bytes // 4, dtype=torch.int32, device=dev)
+        self.o_partial = torch.empty((B, Lq, H, self.num_splits, wl.d_c), dtype=torch.float32, device=dev)
+        self.lse_partial = torch.empty((B, Lq, H, self.num_splits), dtype=torch.float32, device=dev)
+        self.o = torch.empty((B, Lq, H, wl.d_c), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Lq, H), dtype=torch.float32, device=dev)
+        self.u = torch.empty((B, Lq, H, wl.d_v), dtype=st, device=dev)
+
+    def absorb_q(self, stream=None):
+        libmla.mla_absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uk, self.q_cat, stream)
+
+    def decode(self, stream=None):
+        libmla.mla_decode(self.dims, self.q_cat, self.cache, self.block_table, self.seq_lens, self.prob.scale,
+                          self.num_splits, self.workspace, self.o_partial, self.lse_partial, stream)
+
+    def plan(self, stream=None):
+        libmla.mla_decode_plan(self.dims, self.seq_lens, self.num_splits, self.workspace, stream)
+
+    def decode_planned(self, stream=None):
+        libmla.mla_decode_planned(self.dims, self.q_cat, self.cache, self.block_table, self.prob.scale,
+                                  self.num_splits, self.workspace, self.o_partial, self.lse_partial, stream)
+
+    def combine(self, stream=None):
+        libmla.mla_combine(self.dims, self.num_splits, self.o_partial, self.lse_partial, self.o, self.lse, stream)
+
+    def absorb_out(self, stream=None):
+        libmla.mla_absorb_out(self.dims, self.o, self.w_uv, self.u, stream)
+
+    def step(self, stream=None):
+        """One full decode step: absorb_q -> decode -> combine -> absorb_out."""
+        self.absorb_q(stream)
+        self.decode(stream)
+        self.combine(stream)
+        self.absorb_out(stream)
