@@ -61,10 +61,15 @@ int device_cus(int* cus) {
 
 // Which decode kernel serves these dimensions.  MLA_DECODE_KERNEL=generic forces
 // the portable kernel (both are HIP; this is for cross-checking).
-enum class DecodeKind { Generic };
+enum class DecodeKind { Generic, Mfma };
+
+bool force_generic() {
+  const char* e = std::getenv("MLA_DECODE_KERNEL");
+  return e != nullptr && std::strcmp(e, "generic") == 0;
+}
 
 DecodeKind pick_decode(const mla_dims& d) {
-  (void)d;
+  if (!force_generic() && mla::decode_mfma_supported(d)) return DecodeKind::Mfma;
   return DecodeKind::Generic;
 }
 
@@ -85,6 +90,13 @@ int decode_shape(const mla_dims& d, DecodeShape* out) {
       int g = (cus * 8 + row_groups - 1) / row_groups;
       out->grid = g < 1 ? 1 : g;
       out->min_chunk = 1;
+      return MLA_OK;
+    }
+    case DecodeKind::Mfma: {
+      // one 144 KiB-LDS workgroup per CU; a range must amortise loading the
+      // queries (H*Lq rows of 1152 B) against the cache rows it streams
+      out->grid = cus;
+      out->min_chunk = (d.q_len * d.num_heads > 32) ? 4 : 2;
       return MLA_OK;
     }
   }
@@ -180,6 +192,9 @@ hipError_t enqueue_attention(const mla_dims& d, const void* q_cat, const void* k
     case DecodeKind::Generic:
       return mla::launch_decode_generic(d, q_cat, kv_cache, block_table, ws, softmax_scale, num_splits, sh.grid,
                                         o_partial, lse_partial, s);
+    case DecodeKind::Mfma:
+      return mla::launch_decode_mfma(d, q_cat, kv_cache, block_table, ws, softmax_scale, num_splits, sh.grid,
+                                     o_partial, lse_partial, s);
   }
   return hipErrorInvalidValue;
 }

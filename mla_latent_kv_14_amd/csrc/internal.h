@@ -24,4 +24,10 @@ hipError_t launch_combine(const mla_dims& d, int splits, const float* o_part, co
 hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const void* w_uv, void* out,
                                      hipStream_t stream);
 
+// matrix-core decode for bf16, d_c = 512, d_rope = 64 (decode_mfma.hip)
+bool decode_mfma_supported(const mla_dims& d);
+hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
+                              const int32_t* ws, float scale, int splits, int grid, float* o_part, float* lse_part,
+                              hipStream_t stream);
+
 }  // namespace mla

@@ -116,6 +116,24 @@ def test_block_permutation_bit_identical():
     assert torch.equal(u1, r2.u)
 
 
+@pytest.mark.parametrize("name,lens", [("single_4k_bf16", (1, 63, 65, 200, 1000, 4097)),
+                                       ("mtp2_lognormal_bf16", (2, 3, 64, 65, 700, 2049))])
+def test_matrix_core_and_portable_kernels_agree(name, lens, monkeypatch):
+    """Both HIP decode kernels on the same inputs (each is also checked against the oracle)."""
+    wl = workload(name, batch=len(lens), lengths=("fixed", lens))
+    p = make_problem(wl, 51)
+    r1 = _run(p)
+    monkeypatch.setenv("MLA_DECODE_KERNEL", "generic")
+    r2 = _run(p)
+    monkeypatch.delenv("MLA_DECODE_KERNEL")
+    u_ref, _, _ = _oracle(p)
+    assert_parity(to64(r1.u), u_ref, "bf16", "u matrix-core")
+    assert_parity(to64(r2.u), u_ref, "bf16", "u portable")
+    mx, rel = metrics(to64(r1.o), to64(r2.o))
+    say(f"  o matrix-core vs portable: max_abs={mx:.3e} rel={rel:.3e}")
+    assert rel <= 1e-2
+
+
 # ------------------------------------------------------------------ individual entry points
 
 @pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
