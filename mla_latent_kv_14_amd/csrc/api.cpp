@@ -59,13 +59,14 @@ int device_cus(int* cus) {
   return MLA_OK;
 }
 
-// Which decode kernel serves these dimensions.  MLA_DECODE_KERNEL=generic forces
-// the portable kernel (both are HIP; this is for cross-checking).
+// Which kernels serve these dimensions.  MLA_KERNELS=portable forces the
+// portable float32-VALU kernels for every step (both families are HIP; the
+// switch exists to cross-check one against the other).
 enum class DecodeKind { Generic, Mfma };
 
 bool force_generic() {
-  const char* e = std::getenv("MLA_DECODE_KERNEL");
-  return e != nullptr && std::strcmp(e, "generic") == 0;
+  const char* e = std::getenv("MLA_KERNELS");
+  return e != nullptr && std::strcmp(e, "portable") == 0;
 }
 
 DecodeKind pick_decode(const mla_dims& d) {
@@ -125,6 +126,8 @@ int mla_absorb_q(const mla_dims* d, const void* q_nope, const void* q_rope, cons
   if (st != MLA_OK) return st;
   if (!ptr_ok(q_nope) || !ptr_ok(w_uk) || !ptr_ok(q_cat) || (d->d_rope > 0 && !ptr_ok(q_rope)))
     return MLA_ERR_INVALID_ARG;
+  if (!force_generic() && mla::absorb_mfma_supported(*d))
+    return to_status(mla::launch_absorb_q_mfma(*d, q_nope, q_rope, w_uk, q_cat, (hipStream_t)stream));
   return to_status(mla::launch_absorb_q_generic(*d, q_nope, q_rope, w_uk, q_cat, (hipStream_t)stream));
 }
 
@@ -258,6 +261,8 @@ int mla_absorb_out(const mla_dims* d, const float* o_latent, const void* w_uv, v
   int st = check_dims(d);
   if (st != MLA_OK) return st;
   if (!ptr_ok(o_latent) || !ptr_ok(w_uv) || !ptr_ok(out)) return MLA_ERR_INVALID_ARG;
+  if (!force_generic() && mla::absorb_mfma_supported(*d))
+    return to_status(mla::launch_absorb_out_mfma(*d, o_latent, w_uv, out, (hipStream_t)stream));
   return to_status(mla::launch_absorb_out_generic(*d, o_latent, w_uv, out, (hipStream_t)stream));
 }
 

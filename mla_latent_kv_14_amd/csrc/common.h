@@ -21,7 +21,7 @@ constexpr int kPlanTile = 64;
 //   [4] splits  S as passed by the caller
 //   [5] error   0, or 1 + index of the first sequence whose length was out of range
 //   [6] batch   B
-//   [7] reserved
+//   [7] empty   number of sequences with no tokens
 //   [8 .. 8+B]        cu: exclusive prefix sum of tiles per sequence (B + 1 words)
 //   [9+B .. 9+2B)     len: per-sequence length, clamped to [0, MB * block_size]
 constexpr int kWsHeader = 8;
@@ -149,15 +149,18 @@ struct SegmentWalker {
   }
 };
 
-// A sequence with no tokens is visited by no workgroup; workgroup 0 marks all
-// of its splits empty.  `row` is the query row (j * H + h) this lane group owns.
-__device__ __forceinline__ void mark_empty_sequences(const DecodeArgs& a, int row, int lane, int lanes) {
+// A sequence with no tokens is visited by no workgroup: workgroup 0 marks all
+// of its splits empty.  Only runs when the planner counted such sequences;
+// the threads of the workgroup split the (sequence, row) pairs between them.
+__device__ __forceinline__ void mark_empty_sequences(const DecodeArgs& a, int tid, int nthreads) {
+  if (a.ws[7] == 0) return;
   const int32_t* len = a.ws + kWsHeader + a.B + 1;
   const int R = a.Lq * a.H;
-  for (int b = 0; b < a.B; ++b) {
+  for (int i = tid; i < a.B * R; i += nthreads) {
+    const int b = i / R;
     if (len[b] != 0) continue;
-    float* lp = a.lse_part + ((size_t)b * R + row) * a.splits;
-    for (int s = lane; s < a.splits; s += lanes) lp[s] = -INFINITY;
+    float* lp = a.lse_part + (size_t)i * a.splits;
+    for (int s = 0; s < a.splits; ++s) lp[s] = -INFINITY;
   }
 }
 

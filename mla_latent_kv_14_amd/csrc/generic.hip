@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
   const T* cache = (const T*)a.cache;
   const int32_t* len = a.ws + kWsHeader + a.B + 1;
 
-  if (blockIdx.x == 0 && active) mark_empty_sequences(a, row, lane, 64);
+  if (blockIdx.x == 0 && blockIdx.y == 0) mark_empty_sequences(a, threadIdx.x, blockDim.x);
   SegmentWalker walk;
   walk.init(a.ws, blockIdx.x);
   if ((int)blockIdx.x >= walk.groups) return;  // uniform over the workgroup

@@ -30,4 +30,11 @@ hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* 
                               const int32_t* ws, float scale, int splits, int grid, float* o_part, float* lse_part,
                               hipStream_t stream);
 
+// matrix-core absorption GEMMs for bf16, d_nope = d_v = 128, d_c = 512 (absorb_mfma.hip)
+bool absorb_mfma_supported(const mla_dims& d);
+hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
+                                void* q_cat, hipStream_t stream);
+hipError_t launch_absorb_out_mfma(const mla_dims& d, const float* o, const void* w_uv, void* out,
+                                  hipStream_t stream);
+
 }  // namespace mla

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   int32_t* cu = ws + kWsHeader;
   int32_t* len = ws + kWsHeader + B + 1;
 
-  int local_sum = 0, local_max = 0;
+  int local_sum = 0, local_max = 0, local_empty = 0;
   for (int b = threadIdx.x; b < B; b += kPlanThreads) {
     int L = seq_lens[b];
     if (L < q_len || L > max_len) atomicMin(&bad, b);
@@ -60,9 +60,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int n = (L + kPlanTile - 1) / kPlanTile;
     local_sum += n;
     local_max = max(local_max, n);
+    local_empty += (L == 0);
   }
   const int total = block_reduce_sum(local_sum, red);
   const int maxn = block_reduce_max(local_max, red);
+  const int empty = block_reduce_sum(local_empty, red);
 
   int chunk, groups;
   if (splits == 1) {
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     ws[4] = splits;
     ws[5] = (bad == 0x7fffffff) ? 0 : bad + 1;
     ws[6] = B;
-    ws[7] = 0;
+    ws[7] = empty;
   }
 }
 

@@ -123,9 +123,9 @@ def test_matrix_core_and_portable_kernels_agree(name, lens, monkeypatch):
     wl = workload(name, batch=len(lens), lengths=("fixed", lens))
     p = make_problem(wl, 51)
     r1 = _run(p)
-    monkeypatch.setenv("MLA_DECODE_KERNEL", "generic")
+    monkeypatch.setenv("MLA_KERNELS", "portable")
     r2 = _run(p)
-    monkeypatch.delenv("MLA_DECODE_KERNEL")
+    monkeypatch.delenv("MLA_KERNELS")
     u_ref, _, _ = _oracle(p)
     assert_parity(to64(r1.u), u_ref, "bf16", "u matrix-core")
     assert_parity(to64(r2.u), u_ref, "bf16", "u portable")
@@ -136,9 +136,10 @@ def test_matrix_core_and_portable_kernels_agree(name, lens, monkeypatch):
 
 # ------------------------------------------------------------------ individual entry points
 
-@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
-def test_absorb_q_against_oracle(name):
-    wl = workload(name, batch=3, lengths=("fixed", (5, 6, 7)))
+@pytest.mark.parametrize("name,batch", [("tiny_f32", 3), ("single_4k_bf16", 3), ("single_4k_bf16", 70),
+                                        ("mtp2_lognormal_bf16", 40)])
+def test_absorb_q_against_oracle(name, batch):
+    wl = workload(name, batch=batch, lengths=("fixed", tuple(range(5, 5 + batch))))
     p = make_problem(wl, 41)
     r = DecodeRunner(p)
     r.absorb_q()
@@ -151,9 +152,10 @@ def test_absorb_q_against_oracle(name):
     assert (err <= tol).all()
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
-def test_absorb_out_against_oracle(name):
-    wl = workload(name, batch=3, lengths=("fixed", (5, 6, 7)))
+@pytest.mark.parametrize("name,batch", [("tiny_f32", 3), ("single_4k_bf16", 3), ("single_4k_bf16", 70),
+                                        ("mtp2_lognormal_bf16", 40)])
+def test_absorb_out_against_oracle(name, batch):
+    wl = workload(name, batch=batch, lengths=("fixed", tuple(range(5, 5 + batch))))
     p = make_problem(wl, 42)
     r = DecodeRunner(p)
     g = torch.Generator().manual_seed(3)
