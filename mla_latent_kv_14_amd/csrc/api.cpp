@@ -77,6 +77,7 @@ DecodeKind pick_decode(const mla_dims& d) {
 struct DecodeShape {
   int grid;       // workgroups launched along the split axis
   int min_chunk;  // smallest token range (in 64-token tiles) worth one workgroup
+  int ov;         // overhead tiles the planner charges per sequence
 };
 
 int decode_shape(const mla_dims& d, DecodeShape* out) {
@@ -91,13 +92,20 @@ int decode_shape(const mla_dims& d, DecodeShape* out) {
       int g = (cus * 8 + row_groups - 1) / row_groups;
       out->grid = g < 1 ? 1 : g;
       out->min_chunk = 1;
+      out->ov = 0;
       return MLA_OK;
     }
     case DecodeKind::Mfma: {
       // one 144 KiB-LDS workgroup per CU; a range must amortise loading the
-      // queries (H*Lq rows of 1152 B) against the cache rows it streams
+      // queries (H*Lq rows of 1152 B) against the cache rows it streams.
+      // A piece of a sequence costs about as much as streaming
+      //   R * (1152 B of queries + 2048 B of partial result) * 2/3
+      // of cache (the rest overlaps), in 64-row tiles of 73728 B.
+      const int R = d.q_len * d.num_heads;
       out->grid = cus;
-      out->min_chunk = (d.q_len * d.num_heads > 32) ? 4 : 2;
+      out->min_chunk = (R > 32) ? 4 : 2;
+      const int ov = (int)(((int64_t)R * 3200 * 2 / 3 + 36864) / 73728);
+      out->ov = ov < 1 ? 1 : ov;
       return MLA_OK;
     }
   }
@@ -184,7 +192,7 @@ int check_attention_args(const mla_dims* d, const void* q_cat, const void* kv_ca
 
 hipError_t enqueue_plan(const mla_dims& d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
                         const DecodeShape& sh, hipStream_t s) {
-  return mla::launch_plan(d, seq_lens, num_splits, sh.grid, sh.min_chunk, static_cast<int32_t*>(workspace), s);
+  return mla::launch_plan(d, seq_lens, num_splits, sh.grid, sh.min_chunk, sh.ov, static_cast<int32_t*>(workspace), s);
 }
 
 hipError_t enqueue_attention(const mla_dims& d, const void* q_cat, const void* kv_cache, const int32_t* block_table,

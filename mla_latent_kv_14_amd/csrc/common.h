@@ -16,15 +16,23 @@ constexpr int kPlanTile = 64;
 // Workspace layout written by the planner (int32 words):
 //   [0] chunk   tiles per workgroup (>= 1), or 0 in one-sequence-per-workgroup mode
 //   [1] groups  number of workgroups that have work (<= launched grid)
-//   [2] total   total tiles over all sequences
+//   [2] total   length of the schedule line in tiles (real plus overhead tiles)
 //   [3] maxn    tiles of the longest sequence
 //   [4] splits  S as passed by the caller
 //   [5] error   0, or 1 + index of the first sequence whose length was out of range
 //   [6] batch   B
 //   [7] empty   number of sequences with no tokens
-//   [8 .. 8+B]        cu: exclusive prefix sum of tiles per sequence (B + 1 words)
-//   [9+B .. 9+2B)     len: per-sequence length, clamped to [0, MB * block_size]
-constexpr int kWsHeader = 8;
+//   [8] ov      overhead tiles charged at the start of every non-empty sequence
+//   [9 .. 15]   reserved (0)
+//   [16 .. 16+B]      cu: start of each sequence on the schedule line (B + 1 words)
+//   [17+B .. 17+2B)   len: per-sequence length, clamped to [0, MB * block_size]
+// On the schedule line sequence b occupies [cu[b], cu[b+1]): first ov
+// overhead tiles that hold no tokens (they stand for the fixed cost of
+// starting a piece of a sequence: loading its queries, writing its partial
+// result), then its n_b real tiles.  A sequence with no tokens occupies
+// nothing.  Workgroup w owns the line range [w*chunk, (w+1)*chunk), so that
+// cost rather than token count is balanced across workgroups.
+constexpr int kWsHeader = 16;
 inline size_t workspace_words(int batch) { return (size_t)kWsHeader + 2 * (size_t)batch + 1; }
 
 struct DecodeArgs {
@@ -97,9 +105,9 @@ struct Segment {
 // Iterates the segments of workgroup w under the planner's schedule.
 struct SegmentWalker {
   const int32_t* ws;
-  int B, w, chunk, groups, total;
+  int B, w, chunk, groups, total, ov;
   int b;         // current sequence
-  int t_begin;   // workgroup's first tile, t_end its end (chunked mode)
+  int t_begin;   // workgroup's first line tile, t_end its end (chunked mode)
   int t_end;
 
   __device__ __forceinline__ void init(const int32_t* ws_, int w_) {
@@ -109,6 +117,7 @@ struct SegmentWalker {
     groups = ws[1];
     total = ws[2];
     B = ws[6];
+    ov = ws[8];
     if (chunk > 0) {
       t_begin = w * chunk;
       t_end = min(t_begin + chunk, total);
@@ -123,15 +132,17 @@ struct SegmentWalker {
     const int32_t* cu = ws + kWsHeader;
     const int32_t* len = ws + kWsHeader + B + 1;
     if (chunk > 0) {
-      // skip zero-tile sequences
+      // skip sequences that end before the range (empty ones included)
       while (b < B && cu[b + 1] <= t_begin) ++b;
-      if (b >= B || t_begin >= t_end || cu[b] >= t_end) return false;
-      const int c0 = cu[b], c1 = cu[b + 1];
-      const int lo = max(t_begin, c0), hi = min(t_end, c1);
+      if (b >= B || t_begin >= t_end) return false;
+      const int c1 = cu[b + 1];
+      const int rs = cu[b] + ov;  // first real tile of b (b is not empty here)
+      if (rs >= t_end) return false;
+      const int lo = max(t_begin, rs), hi = min(t_end, c1);
       s.b = b;
-      s.tok_begin = (lo - c0) * kPlanTile;
-      s.tok_end = min((hi - c0) * kPlanTile, len[b]);
-      const int first = c0 / chunk;
+      s.tok_begin = (lo - rs) * kPlanTile;
+      s.tok_end = min((hi - rs) * kPlanTile, len[b]);
+      const int first = rs / chunk;
       s.split = w - first;
       s.nsplits = (c1 - 1) / chunk - first + 1;
       t_begin = hi;
@@ -148,6 +159,16 @@ struct SegmentWalker {
     return true;
   }
 };
+
+// Workgroups are dispatched to the eight XCDs of the chip in turn (workgroup p
+// runs on XCD p mod 8).  Neighbouring ranges of the schedule usually share a
+// sequence (its queries are read by both), so the schedule index is chosen to
+// keep neighbours on one XCD and its L2: XCD x takes a contiguous block of
+// schedule indices.
+__device__ __forceinline__ int xcd_local_index(int p, int grid) {
+  const int q = grid >> 3, r = grid & 7, x = p & 7, k = p >> 3;
+  return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
 
 // A sequence with no tokens is visited by no workgroup: workgroup 0 marks all
 // of its splits empty.  Only runs when the planner counted such sequences;

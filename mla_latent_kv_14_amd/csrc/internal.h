@@ -9,7 +9,7 @@
 namespace mla {
 
 // planner (plan.hip)
-hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk,
+hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk, int ov,
                        int32_t* ws, hipStream_t stream);
 
 // portable kernels for any supported shape (generic.hip)

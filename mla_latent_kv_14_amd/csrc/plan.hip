@@ -1,11 +1,13 @@
 // Device-side work planner for split-KV decode.
 //
-// One workgroup turns the per-sequence lengths into a token-balanced
-// schedule: sequences are cut into 64-token tiles, the tiles of all sequences
-// are laid end to end, and workgroup w of the attention kernel takes tiles
-// [w*chunk, (w+1)*chunk).  A workgroup's range may span several sequences and
-// a sequence may span several workgroups; each (sequence, workgroup) piece is
-// one split.  chunk is the smallest value that (a) fits the whole range in the
+// One workgroup turns the per-sequence lengths into a cost-balanced
+// schedule: sequences are cut into 64-token tiles, each non-empty sequence is
+// preceded by ov overhead tiles (the fixed cost of a piece: its queries and
+// its partial result), everything is laid end to end on one line, and
+// workgroup w of the attention kernel takes line tiles [w*chunk, (w+1)*chunk).
+// A workgroup's range may span several sequences and a sequence may span
+// several workgroups; each (sequence, workgroup) piece with real tiles is one
+// split.  chunk is the smallest value that (a) fits the whole line in the
 // launched grid, (b) keeps every sequence within num_splits pieces and (c) is
 // at least the kernel's minimum useful range.
 #include "common.h"
@@ -41,7 +43,7 @@ __device__ __forceinline__ int block_reduce_max(int v, int* red) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens, int B, int q_len,
-                                                            int max_len, int splits, int grid, int min_chunk,
+                                                            int max_len, int splits, int grid, int min_chunk, int ov,
                                                             int32_t* __restrict__ ws) {
   __shared__ int red[kPlanThreads / 64];
   __shared__ int scan[kPlanThreads];
@@ -58,7 +60,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     L = min(max(L, 0), max_len);
     len[b] = L;
     const int n = (L + kPlanTile - 1) / kPlanTile;
-    local_sum += n;
+    local_sum += n + (n > 0 ? ov : 0);
     local_max = max(local_max, n);
     local_empty += (L == 0);
   }
@@ -81,7 +83,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   int offset = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int b = base + threadIdx.x;
-    const int n = (b < B) ? (len[b] + kPlanTile - 1) / kPlanTile : 0;
+    int n = (b < B) ? (len[b] + kPlanTile - 1) / kPlanTile : 0;
+    n += (n > 0) ? ov : 0;
     __syncthreads();
     scan[threadIdx.x] = n;
     __syncthreads();
@@ -105,16 +108,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     ws[5] = (bad == 0x7fffffff) ? 0 : bad + 1;
     ws[6] = B;
     ws[7] = empty;
+    ws[8] = ov;
+    for (int k = 9; k < kWsHeader; ++k) ws[k] = 0;
   }
 }
 
 }  // namespace
 
-hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk,
+hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk, int ov,
                        int32_t* ws, hipStream_t stream) {
   const int max_len = d.max_blocks_per_seq * d.block_size;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, d.batch, d.q_len, max_len,
-                     splits, grid, min_chunk, ws);
+                     splits, grid, min_chunk, ov, ws);
   return hipGetLastError();
 }
 

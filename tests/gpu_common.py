@@ -55,27 +55,37 @@ def assert_parity(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
 PLAN_TILE = 64
 
 
+WS_HEADER = 16
+
+
 def replay_schedule(ws: np.ndarray):
     """Host replay of the planner's schedule read back from the workspace.
 
-    Returns (header dict, list of segments (w, b, tok_begin, tok_end, split, nsplits)).
+    Header words: chunk, groups, total, maxn, splits, error, B, empty, ov.
+    Sequence b occupies [cu[b], cu[b+1]) of the schedule line: ov overhead
+    tiles (none for an empty sequence), then its real tiles.  Workgroup w
+    owns line tiles [w*chunk, (w+1)*chunk).
+    Returns (header dict, list of segments (w, b, tok_begin, tok_end, split, nsplits), lengths).
     """
-    chunk, groups, total, maxn, splits, err, B = (int(x) for x in ws[:7])
-    cu = ws[8:8 + B + 1].astype(np.int64)
-    lens = ws[9 + B:9 + 2 * B].astype(np.int64)
+    chunk, groups, total, maxn, splits, err, B, empty, ov = (int(x) for x in ws[:9])
+    cu = ws[WS_HEADER:WS_HEADER + B + 1].astype(np.int64)
+    lens = ws[WS_HEADER + B + 1:WS_HEADER + 2 * B + 1].astype(np.int64)
     segs = []
     if chunk > 0:
         for w in range(groups):
             t0, t1 = w * chunk, min((w + 1) * chunk, total)
             for b in range(B):
-                lo, hi = max(t0, cu[b]), min(t1, cu[b + 1])
+                if cu[b + 1] == cu[b]:
+                    continue
+                rs = cu[b] + ov
+                lo, hi = max(t0, rs), min(t1, cu[b + 1])
                 if lo >= hi:
                     continue
-                first = cu[b] // chunk
-                segs.append((w, b, int((lo - cu[b]) * PLAN_TILE), int(min((hi - cu[b]) * PLAN_TILE, lens[b])),
+                first = rs // chunk
+                segs.append((w, b, int((lo - rs) * PLAN_TILE), int(min((hi - rs) * PLAN_TILE, lens[b])),
                              int(w - first), int((cu[b + 1] - 1) // chunk - first + 1)))
     else:
         for b in range(B):
             segs.append((b % groups, b, 0, int(lens[b]), 0, 1))
-    hdr = dict(chunk=chunk, groups=groups, total=total, maxn=maxn, splits=splits, error=err, B=B)
+    hdr = dict(chunk=chunk, groups=groups, total=total, maxn=maxn, splits=splits, error=err, B=B, empty=empty, ov=ov)
     return hdr, segs, lens
