@@ -2,8 +2,8 @@
 """Decode-step benchmark for libmla on one MI355X.
 
 A step is one pass of the whole hot path over one batch: plan, absorb_q,
-split-KV attention, log-sum-exp combine, absorb_out, for every sequence of
-the workload.  Inputs are seeded synthetic tensors already resident in HBM.
+split-KV attention, then the log-sum-exp combine and absorb_out (one fused
+call), for every sequence of the workload.  Inputs are seeded synthetic tensors already resident in HBM.
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -142,8 +142,8 @@ def main():
     stream = torch.cuda.current_stream()
     log(f"bench: B={wl.batch} H={wl.heads} Lq={wl.q_len} tokens={prob.total_tokens} splits={r.num_splits}")
 
-    calls = [("plan", r.plan), ("absorb_q", r.absorb_q), ("decode", r.decode_planned), ("combine", r.combine),
-             ("absorb_out", r.absorb_out)]
+    calls = [("plan", r.plan), ("absorb_q", r.absorb_q), ("decode", r.decode_planned),
+             ("combine_absorb_out", r.combine_absorb_out)]
     for _ in range(args.warmup):
         for _, fn in calls:
             fn()

@@ -162,6 +162,26 @@ int mla_combine(const mla_dims* dims, int32_t num_splits, const float* o_partial
  * [B,Lq,H,d_v] storage type. */
 int mla_absorb_out(const mla_dims* dims, const float* o_latent, const void* w_uv, void* out, void* stream);
 
+/* mla_combine and mla_absorb_out in one call (the guide's section 3,
+ * Absorbing W^UV, applied to the merged latent output):
+ *   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s,
+ *   u[b,j,h,v] = sum_c w_uv[h,v,c] * o[b,j,h,c]
+ * Arguments as for the two calls: o_partial/lse_partial as written by
+ * mla_decode, w_uv [H,d_v,d_c] storage type, out [B,Lq,H,d_v] storage type.
+ * o_latent [B,Lq,H,d_c] float32 and lse [B,Lq,H] float32 are optional
+ * outputs (NULL to skip).  When mla_combine_absorb_out_fused() returns 1 for
+ * these dims and split count, one kernel merges each tile of rows on chip and
+ * the merged latent output is only written if o_latent is given; otherwise the
+ * call runs the two kernels and needs o_latent as their intermediate
+ * (MLA_ERR_UNSUPPORTED if it is NULL). */
+int mla_combine_absorb_out(const mla_dims* dims, int32_t num_splits, const float* o_partial, const float* lse_partial,
+                           const void* w_uv, void* out, float* o_latent, float* lse, void* stream);
+
+/* 1 if mla_combine_absorb_out runs as one fused kernel for these dims and
+ * split count (bf16 storage, d_c = 512, d_nope = d_v = 128, at most 64
+ * splits), else 0 (also for invalid arguments).  Host only. */
+int mla_combine_absorb_out_fused(const mla_dims* dims, int32_t num_splits);
+
 /* Static description of a status code. */
 const char* mla_status_str(int status);
 

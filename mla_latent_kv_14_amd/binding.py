@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
         "mla_decode_planned": [D, P, P, P, F32, I32, P, SZ, P, P, P],
         "mla_combine": [D, I32, P, P, P, P, P],
         "mla_absorb_out": [D, P, P, P, P],
+        "mla_combine_absorb_out": [D, I32, P, P, P, P, P, P, P],
+        "mla_combine_absorb_out_fused": [D, I32],
         "mla_version": [],
     }
     for name, args in sig.items():
@@ -202,3 +204,20 @@ def mla_absorb_out(dims, o_latent, w_uv, out, stream=None):
     _check("mla_absorb_out", load().mla_absorb_out(
         ctypes.byref(d), _ptr(o_latent, "o_latent", torch.float32, rows * d.d_c),
         _ptr(w_uv, "w_uv", st, d.num_heads * d.d_v * d.d_c), _ptr(out, "out", st, rows * d.d_v), _stream(stream)))
+
+
+def mla_combine_absorb_out(dims, num_splits, o_partial, lse_partial, w_uv, out, o_latent=None, lse=None,
+                           stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    _check("mla_combine_absorb_out", load().mla_combine_absorb_out(
+        ctypes.byref(d), int(num_splits), _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits),
+        _ptr(w_uv, "w_uv", st, d.num_heads * d.d_v * d.d_c), _ptr(out, "out", st, rows * d.d_v),
+        _ptr(o_latent, "o_latent", torch.float32, rows * d.d_c) if o_latent is not None else None,
+        _ptr(lse, "lse", torch.float32, rows) if lse is not None else None, _stream(stream)))
+
+
+def mla_combine_absorb_out_fused(dims, num_splits) -> bool:
+    return bool(load().mla_combine_absorb_out_fused(ctypes.byref(dims), int(num_splits)))
+

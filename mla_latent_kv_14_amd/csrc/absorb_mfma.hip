@@ -52,6 +52,17 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
   uint4 a_cur[kDN / 16];
   load_a(0, a_cur);
 
+  // the RoPE part of each row is copied unchanged, 16 B per thread, spread
+  // over the d_c / 128 workgroups of head h (d_r is a multiple of 8)
+  {
+    const int per_row = d_r / 8, nchunk = M * per_row;
+    for (int i = nq * kThreads + tid; i < nchunk; i += kThreads * (kDC / kNQ)) {
+      const int m = i / per_row, k = i - m * per_row;
+      *reinterpret_cast<uint4*>(q_cat + ((size_t)m * H + h) * D + kDC + 8 * k) =
+          *reinterpret_cast<const uint4*>(q_rope + ((size_t)m * H + h) * d_r + 8 * k);
+    }
+  }
+
   const uint16_t* w = w_uk + (size_t)h * kDN * kDC + nq * kNQ;
   uint4 wv[(kDN * kNQ / 8) / kThreads];
 #pragma unroll
@@ -105,12 +116,6 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
     }
   }
 
-  if (nq == 0) {  // the RoPE part of each row is copied unchanged
-    for (int i = tid; i < M * d_r; i += kThreads) {
-      const int m = i / d_r, k = i % d_r;
-      q_cat[((size_t)m * H + h) * D + kDC + k] = q_rope[((size_t)m * H + h) * d_r + k];
-    }
-  }
 }
 
 // ------------------------------------------------------------------ absorb_out
@@ -179,6 +184,113 @@ __global__ __launch_bounds__(kThreads) void absorb_out_mfma(const float* __restr
   }
 }
 
+
+// ------------------------------------------------------------ combine + absorb_out
+// The log-sum-exp merge of the split partials fused with the W_UV product, so
+// that the merged latent output never leaves the chip:
+//   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s,  u = W_UV[h] o.
+// grid (H, ceil(M / 32)); the 32 rows of a workgroup are merged straight into
+// the bf16 hi/lo LDS tile of absorb_out_mfma.  Splits with lse_s = -inf are
+// skipped (their o_s is never read).  o_latent and lse are written when given.
+constexpr int kMaxFusedSplits = 64;
+
+__global__ __launch_bounds__(kThreads) void combine_out_mfma(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             const uint16_t* __restrict__ w_uv,
+                                                             uint16_t* __restrict__ out, float* __restrict__ o_latent,
+                                                             float* __restrict__ lse_out, int M, int H, int S) {
+  __shared__ __attribute__((aligned(16))) uint8_t ot[2][32 * kDC * 2];
+  __shared__ float wts[32][kMaxFusedSplits];
+  const int h = blockIdx.x, m0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
+
+  // every B operand (W_UV rows) of this wave is requested first
+  const int v = 32 * wave + (lane & 31);
+  const uint16_t* wrow = w_uv + ((size_t)h * kDV + v) * kDC + 8 * hi;
+  uint4 bw[kDC / 16];
+#pragma unroll
+  for (int ks = 0; ks < kDC / 16; ++ks) bw[ks] = *reinterpret_cast<const uint4*>(wrow + 16 * ks);
+
+  // split weights: 8 lanes per row
+  {
+    const int r = tid >> 3, j = tid & 7, m = m0 + r;
+    const float* lp = lse_part + ((size_t)min(m, M - 1) * H + h) * S;
+    const float total = split_lse(lp, S, j);
+    for (int s2 = j; s2 < S; s2 += 8) {
+      const float ls = lp[s2];
+      wts[r][s2] = (ls == -INFINITY || m >= M) ? 0.f : expf(ls - total);
+    }
+    if (lse_out != nullptr && j == 0 && m < M) lse_out[(size_t)m * H + h] = total;
+  }
+  __syncthreads();
+
+  // merge: thread (row r, lane j of 8) owns float4 columns j + 8 k, k < 16
+  {
+    const int r = tid >> 3, j = tid & 7, m = m0 + r;
+    float4 acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m < M) {
+      const float4* src = reinterpret_cast<const float4*>(o_part + ((size_t)m * H + h) * S * kDC);
+      for (int s2 = 0; s2 < S; ++s2) {
+        const float wgt = wts[r][s2];
+        if (wgt == 0.f) continue;
+        float4 x[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x[k] = src[(size_t)s2 * (kDC / 4) + j + 8 * k];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          acc[k].x = fmaf(wgt, x[k].x, acc[k].x);
+          acc[k].y = fmaf(wgt, x[k].y, acc[k].y);
+          acc[k].z = fmaf(wgt, x[k].z, acc[k].z);
+          acc[k].w = fmaf(wgt, x[k].w, acc[k].w);
+        }
+      }
+      if (o_latent != nullptr) {
+        float4* dst = reinterpret_cast<float4*>(o_latent + ((size_t)m * H + h) * kDC);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dst[j + 8 * k] = acc[k];
+      }
+    }
+    // float4 column f = j + 8 k covers half of 16-B chunk c = f / 2 (8 bytes of bf16)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int f = j + 8 * k, c = f >> 1;
+      const float e[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint16_t h0 = f32_to_bf16_bits(e[2 * q]), h1 = f32_to_bf16_bits(e[2 * q + 1]);
+        const uint16_t l0 = f32_to_bf16_bits(e[2 * q] - bf16_bits_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16_bits(e[2 * q + 1] - bf16_bits_to_f32(h1));
+        hw[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      const int off = r * 1024 + ((c ^ (r & 15)) * 16) + 8 * (f & 1);
+      *reinterpret_cast<uint2*>(&ot[0][off]) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(&ot[1][off]) = make_uint2(lw[0], lw[1]);
+    }
+  }
+  __syncthreads();
+
+  const int r = lane & 31;
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kDC / 16; ++ks) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bw[ks]);
+    const int off = r * 1024 + (((2 * ks + hi) ^ (r & 15)) * 16);
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&ot[0][off]);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ot[1][off]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int m = m0 + 8 * (rr >> 2) + 4 * hi + (rr & 3);
+    if (m < M) out[((size_t)m * H + h) * kDV + v] = f32_to_bf16_bits(acc[rr]);
+  }
+}
+
 }  // namespace
 
 bool absorb_mfma_supported(const mla_dims& d) {
@@ -191,6 +303,16 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const voi
   hipLaunchKernelGGL(absorb_q_mfma, dim3(d.num_heads, kDC / kNQ), dim3(kThreads), 0, stream,
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, (uint16_t*)q_cat, M,
                      d.num_heads, d.d_rope);
+  return hipGetLastError();
+}
+
+int combine_out_max_splits() { return kMaxFusedSplits; }
+
+hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o_part, const float* lse_part,
+                                   const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream) {
+  const int M = d.batch * d.q_len;
+  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreads), 0, stream, o_part, lse_part,
+                     (const uint16_t*)w_uv, (uint16_t*)out, o_latent, lse, M, d.num_heads, splits);
   return hipGetLastError();
 }
 

@@ -274,4 +274,29 @@ int mla_absorb_out(const mla_dims* d, const float* o_latent, const void* w_uv, v
   return to_status(mla::launch_absorb_out_generic(*d, o_latent, w_uv, out, (hipStream_t)stream));
 }
 
+int mla_combine_absorb_out(const mla_dims* d, int32_t num_splits, const float* o_partial, const float* lse_partial,
+                           const void* w_uv, void* out, float* o_latent, float* lse, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(o_partial) || !ptr_ok(lse_partial) || !ptr_ok(w_uv) || !ptr_ok(out) ||
+      (o_latent != nullptr && !aligned16(o_latent)) || (lse != nullptr && !aligned16(lse)))
+    return MLA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (!force_generic() && mla::absorb_mfma_supported(*d) && num_splits <= mla::combine_out_max_splits())
+    return to_status(mla::launch_combine_out_mfma(*d, num_splits, o_partial, lse_partial, w_uv, out, o_latent, lse, s));
+  // two-kernel route: the merged latent output goes through o_latent
+  if (o_latent == nullptr) return MLA_ERR_UNSUPPORTED;
+  hipError_t e = mla::launch_combine(*d, num_splits, o_partial, lse_partial, o_latent, lse, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (!force_generic() && mla::absorb_mfma_supported(*d))
+    return to_status(mla::launch_absorb_out_mfma(*d, o_latent, w_uv, out, s));
+  return to_status(mla::launch_absorb_out_generic(*d, o_latent, w_uv, out, s));
+}
+
+int mla_combine_absorb_out_fused(const mla_dims* d, int32_t num_splits) {
+  if (check_dims(d) != MLA_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  return (!force_generic() && mla::absorb_mfma_supported(*d) && num_splits <= mla::combine_out_max_splits()) ? 1 : 0;
+}
+
 }  // extern "C"

@@ -81,6 +81,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Log-sum-exp of one row's split values lp[0..S) (natural log; -inf entries
+// are empty splits): every lane of an aligned group of 8 lanes returns the
+// same value; j is the lane's index in its group.  The summation order is
+// fixed (eight strided partial sums combined by a butterfly; float addition
+// is commutative, so all eight lanes agree), which makes every kernel that
+// merges splits produce bit-identical weights exp(lse_s - lse).
+__device__ __forceinline__ float split_lse(const float* lp, int S, int j) {
+  float mx = -INFINITY;
+  for (int s = j; s < S; s += 8) mx = fmaxf(mx, lp[s]);
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (mx == -INFINITY) return -INFINITY;
+  float z = 0.f;
+  for (int s = j; s < S; s += 8) z += expf(lp[s] - mx);
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off, 64);
+  return mx + logf(z);
+}
+
 // ---- schedule lookups shared by every decode kernel ----------------------------------
 
 // Largest b in [0, B) with cu[b] <= tile (cu is non-decreasing, cu[0] = 0).

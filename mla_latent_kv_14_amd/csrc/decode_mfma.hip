@@ -63,6 +63,9 @@ constexpr int kKSteps = kD / 16;         // 36
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kHeadroom = 64.0f;  // log2 units a score may exceed the reference max
+// LDS operand ring depth of the score and latent-sum loops (reads issued this
+// many steps ahead of their MFMA; deeper rings measured slower)
+constexpr int kOperandAhead = 4;
 
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
@@ -153,33 +156,48 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   walk.init(ws, w);
   if (w >= walk.groups) return;
 
-  int kbase[4];
-  {
-    const int r = lane & 31, g = swz(r);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) kbase[v] = r * kRowBytes + 16 * ((2 * v + hi) ^ g);
-  }
-  int vbase[2][2];
-  {
-    const int g16 = lane >> 4, j16 = lane & 15;
+  // Per-lane LDS byte offsets inside a sub-tile, recomputed per sub-tile from
+  // the lane index (a few integer ops) instead of being held in registers:
+  //   score operand v (logical chunk 2 v + hi of row r = lane & 31):
+  //     r * 1152 + 16 ((2 v + hi) ^ g(r))
+  //   transpose operand (h, mb parity par): this lane supplies row
+  //     16 kk + 8 h + tr_row, columns 32 mb + tr_col .. +3; with
+  //     sw = g(tr_row) ^ (h << 1) the swizzled chunk is
+  //     4 (mb ^ (sw >> 2)) + (y ^ (sw & 3)), y = tr_col >> 3, and the mb ^ bit
+  //     swap is folded into one base per (h, mb parity).
+  // (the empty asm hides that the lane index is loop-invariant, so that the
+  // compiler recomputes rather than hoists and holds these values)
+  auto opaque_lane = [&]() {
+    int l = lane;
+    __asm__ volatile("" : "+v"(l));
+    return l;
+  };
+  auto kbase = [&](int v) {
+    const int ln = opaque_lane();
+    const int r = ln & 31;
+    return r * kRowBytes + 16 * ((2 * v + (ln >> 5)) ^ swz(r));
+  };
+  auto vbase = [&](int h, int par) {
+    const int ln = opaque_lane();
+    const int g16 = ln >> 4, j16 = ln & 15;
     const int tr_row = 4 * (g16 >> 1) + (j16 >> 2);
     const int y = 2 * (g16 & 1) + ((j16 & 3) >> 1);
     const int s2 = (swz(tr_row) >> 2) & 1;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int sw = swz(tr_row) ^ (h << 1);
-      const int b0 = tr_row * kRowBytes + 16 * (y ^ (sw & 3)) + 8 * (j16 & 1) + 64 * (cg * MB);
-#pragma unroll
-      for (int par = 0; par < 2; ++par) vbase[h][par] = b0 + (s2 ? (par ? -64 : 64) : 0);
-    }
-  }
-  int dma_src[kDmaPerWave];
-#pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int q = (wave + 4 * i) * 64 + lane;
-    const int r = q / kChunks, pc = q - r * kChunks;
-    dma_src[i] = r * kRowBytes + (pc ^ swz(r)) * 16;
-  }
+    const int sw = swz(tr_row) ^ (h << 1);
+    const int b0 = tr_row * kRowBytes + 16 * (y ^ (sw & 3)) + 8 * (j16 & 1) + 64 * (cg * MB);
+    return b0 + (s2 ? (par ? -64 : 64) : 0);
+  };
+  // Source offset inside a sub-tile of this lane's part of copy piece i:
+  // the piece fills physical chunk q = 64 (wave + 4 i) + lane, which holds
+  // logical chunk (q mod 72) ^ g(r) of row r = q / 72.  Recomputed per copy
+  // (a few integer ops) rather than kept in nine registers.
+  const int q_lane = wave * 64 + lane;
+  auto dma_src = [&](int i) {
+    const int q = q_lane + 256 * i;
+    const int r = (q * 1821) >> 17;  // q / 72 for 0 <= q < 2304
+    const int pc = q - r * kChunks;
+    return r * kRowBytes + ((pc ^ swz(r)) << 4);
+  };
 
   // Block-table window of a segment: lane j holds the physical block of the
   // segment's j-th block (j < 64).  The next segment's window is requested
@@ -201,19 +219,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     const int32_t* trow = table + (size_t)b * a.max_blocks;
     const int j0 = seg.tok_begin / a.block_size;
 
-    auto issue = [&](int sub) {
+    // Copy of one sub-tile: the source row address (uniform) and this wave's
+    // nine 1 KiB pieces of it.  The pieces of a sub-tile copied during the
+    // score loop are spread over its MFMAs so that the address unit works in
+    // the background instead of stalling the wave.
+    auto tile_src = [&](int sub) -> const uint8_t* {
       const int t = seg.tok_begin + sub * kSub;
       const int j = t / a.block_size - j0;
       int blk = (j < 64) ? __builtin_amdgcn_readlane(tv, j) : trow[t / a.block_size];
       blk = min(max(blk, 0), a.num_blocks - 1);
-      const uint8_t* base = cache + ((size_t)blk * a.block_size + (t % a.block_size)) * kRowBytes;
+      return cache + ((size_t)blk * a.block_size + (t % a.block_size)) * kRowBytes;
+    };
+    auto dma = [&](const uint8_t* base, int sub, int i) {
       const uint32_t dst = (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes + wave * 1024;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + 4096 * i);
+      __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_src(i)), "s"(base), "{m0}"(m0)
+                       : "memory");
+    };
+    auto issue = [&](int sub) {
+      const uint8_t* base = tile_src(sub);
 #pragma unroll
-      for (int i = 0; i < kDmaPerWave; ++i) {
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + 4096 * i);
-        __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_src[i]), "s"(base), "{m0}"(m0)
-                         : "memory");
-      }
+      for (int i = 0; i < kDmaPerWave; ++i) dma(base, sub, i);
     };
     // rows of a sub-tile past the sequence end hold unspecified data: zero them
     auto fix_partial = [&](int sub) {
@@ -262,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       auto kbases = [&](int stage, int* kb) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          kb[v] = stage * kSubBytes + kbase[v];
+          kb[v] = stage * kSubBytes + kbase(v);
           __asm__ volatile("" : "+v"(kb[v]));
         }
       };
@@ -301,7 +327,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
           block_sync();  // sub-tile i+1 landed; every wave is past PV(i-1)
           fix_partial(i + 1);
         }
-        if (i + 3 < n_sub) issue(i + 3);
+        // Sub-tile i+3 is copied during the score loop below, one 1 KiB piece
+        // every fourth MFMA: a wave can queue only a few copies, and a burst of
+        // nine would stall it for their whole transfer.
+        const int copy_on = (i + 3 < n_sub) ? 1 : 0;
+        const uint8_t* copy_src = copy_on ? tile_src(i + 3) : cache;
 
         // masking of sub-tile i (rare: only where some row's last visible token falls inside)
         if (t0 + kSub > lim_all) {
@@ -342,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         if (nxt) {
           int kb[4];
           kbases((i + 1) & (kStages - 1), kb);
-          constexpr int kAhead = 4;
+          constexpr int kAhead = kOperandAhead;
           bf16x8 kop[kAhead];
 #pragma unroll
           for (int ks = 0; ks < kAhead - 1; ++ks) kop[ks] = kload(kb, ks);
@@ -352,6 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
             if (ks == 0) mfma_v0(sn, kop[0], q[0]);
             else mfma_v(sn, kop[ks % kAhead], q[ks]);
             if (ks < kPieces) piece(ks);
+            if (ks % 4 == 2 && copy_on > 0) dma(copy_src, i + 3, ks / 4);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
@@ -367,11 +398,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int par = 0; par < 2; ++par) {
-              vb[h][par] = (i & (kStages - 1)) * kSubBytes + vbase[h][par];
+              vb[h][par] = (i & (kStages - 1)) * kSubBytes + vbase(h, par);
               __asm__ volatile("" : "+v"(vb[h][par]));
             }
           constexpr int kSteps = 2 * MB;
-          constexpr int kAhead = 4;
+          constexpr int kAhead = kOperandAhead;
           bf16x8 vop[kAhead];
           auto vload = [&](int st) {
             const int mb = st >> 1, kk = st & 1;

@@ -179,20 +179,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
   const int row = blockIdx.x * (kThreads / 64) + wave;
   if (row >= rows) return;
   const float* lp = lse_part + (size_t)row * S;
-  float m = -INFINITY;
-  for (int s = lane; s < S; s += 64) m = fmaxf(m, lp[s]);
-  m = wave_max(m);
+  const float total = split_lse(lp, S, lane & 7);
   float4* o4 = reinterpret_cast<float4*>(o + (size_t)row * d_c);
   const int n4 = d_c / 4;
-  if (m == -INFINITY) {
+  if (total == -INFINITY) {
     for (int c = lane; c < n4; c += 64) o4[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lse && lane == 0) lse[row] = -INFINITY;
     return;
   }
-  float z = 0.f;
-  for (int s = lane; s < S; s += 64) z += expf(lp[s] - m);
-  z = wave_sum(z);
-  const float total = m + logf(z);
   const float4* src = reinterpret_cast<const float4*>(o_part + (size_t)row * S * d_c);
   for (int c = lane; c < n4; c += 64) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

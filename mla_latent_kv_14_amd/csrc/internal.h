@@ -36,5 +36,10 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const voi
                                 void* q_cat, hipStream_t stream);
 hipError_t launch_absorb_out_mfma(const mla_dims& d, const float* o, const void* w_uv, void* out,
                                   hipStream_t stream);
+// fused log-sum-exp merge + W_UV product (same support as the MFMA absorb
+// kernels, and at most combine_out_max_splits() splits)
+int combine_out_max_splits();
+hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o_part, const float* lse_part,
+                                   const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream);
 
 }  // namespace mla

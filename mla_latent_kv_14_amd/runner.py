@@ -66,6 +66,14 @@ class DecodeRunner:
     def absorb_out(self, stream=None):
         libmla.mla_absorb_out(self.dims, self.o, self.w_uv, self.u, stream)
 
+    def combine_absorb_out(self, keep_latent=False, stream=None):
+        """Merge the splits and apply W_UV in one call (the latent output is
+        written to self.o only when asked, or when the call is not fused)."""
+        fused = libmla.mla_combine_absorb_out_fused(self.dims, self.num_splits)
+        libmla.mla_combine_absorb_out(self.dims, self.num_splits, self.o_partial, self.lse_partial, self.w_uv, self.u,
+                                      self.o if (keep_latent or not fused) else None,
+                                      self.lse if (keep_latent or not fused) else None, stream)
+
     def step(self, stream=None):
         """One full decode step: absorb_q -> decode -> combine -> absorb_out."""
         self.absorb_q(stream)

@@ -107,6 +107,31 @@ def test_absorb_null_and_misaligned():
     assert _call("mla_combine", ctypes.byref(d), 2, P(FAKE), P(FAKE), P(FAKE), P(FAKE + 4), None) == -1
 
 
+def test_combine_absorb_out_args():
+    d = _dims()
+    f = "mla_combine_absorb_out"
+    assert _call(f, ctypes.byref(d), 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None) == -1
+    assert _call(f, ctypes.byref(d), 2, None, P(FAKE), P(FAKE), P(FAKE), None, None, None) == -1
+    assert _call(f, ctypes.byref(d), 2, P(FAKE), P(FAKE), P(FAKE), None, None, None, None) == -1
+    assert _call(f, ctypes.byref(d), 2, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE + 4), None, None) == -1
+    assert _call(f, ctypes.byref(d), 2, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, P(FAKE + 4), None) == -1
+    # float32 storage has no fused kernel: without o_latent there is no intermediate
+    d32 = _dims(dtype=0, d_c=64, d_rope=16, d_nope=32, d_v=32)
+    assert _call(f, ctypes.byref(d32), 2, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, None, None) == -2
+
+
+def test_combine_absorb_out_fused_predicate():
+    lib = libmla.load()
+    d = _dims(dtype=libmla.MLA_BF16, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128, block_size=64)
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 8) == 1
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 64) == 1
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 65) == 0
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 0) == 0
+    d32 = _dims(dtype=0, d_c=64, d_rope=16, d_nope=32, d_v=32)
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d32), 8) == 0
+    assert lib.mla_combine_absorb_out_fused(None, 8) == 0
+
+
 def test_num_splits_args():
     d = _dims()
     out = ctypes.c_int32(0)

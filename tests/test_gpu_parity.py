@@ -35,9 +35,15 @@ def _oracle(prob, select=None):
 
 
 def _run(prob, num_splits=None):
+    """Four-call step, then the fused merge + W_UV call, which must give the same u bit for bit."""
     r = DecodeRunner(prob, num_splits=num_splits)
     r.step()
     torch.cuda.synchronize()
+    u_steps = r.u.clone()
+    r.u.fill_(0)
+    r.combine_absorb_out()
+    torch.cuda.synchronize()
+    assert torch.equal(r.u, u_steps), "mla_combine_absorb_out differs from mla_combine + mla_absorb_out"
     return r
 
 
@@ -169,6 +175,25 @@ def test_absorb_out_against_oracle(name, batch):
     err = np.abs(got - ref)
     say(f"  absorb_out {name}: max_abs={err.max():.3e}")
     assert (err <= tol).all()
+
+
+@pytest.mark.parametrize("name,lens", [("tiny_f32", (37, 200)), ("single_4k_bf16", (1, 70, 640, 3000))])
+def test_combine_absorb_out_keeps_latent(name, lens):
+    """With o_latent and lse requested, the one-call route writes exactly what mla_combine writes."""
+    wl = workload(name, batch=len(lens), lengths=("fixed", lens))
+    r = DecodeRunner(make_problem(wl, 51), num_splits=5)
+    r.absorb_q()
+    r.decode()
+    r.combine()
+    r.absorb_out()
+    torch.cuda.synchronize()
+    o1, l1, u1 = r.o.clone(), r.lse.clone(), r.u.clone()
+    r.o.fill_(7.0)
+    r.lse.fill_(7.0)
+    r.u.fill_(0)
+    r.combine_absorb_out(keep_latent=True)
+    torch.cuda.synchronize()
+    assert torch.equal(r.o, o1) and torch.equal(r.lse, l1) and torch.equal(r.u, u1)
 
 
 def test_combine_against_oracle():
