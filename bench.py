@@ -120,6 +120,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="time HIP-graph replays instead of eager launches")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -149,24 +150,44 @@ def main():
             fn()
     torch.cuda.synchronize()
     log("bench: warmup done")
-
     K = args.steps
+
+    # per-call breakdown: eager calls bracketed by events on the library's stream
     ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
           for n, _ in calls}
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
     for i in range(K):
         for n, fn in calls:
             ev[n][i][0].record(stream)
             fn()
             ev[n][i][1].record(stream)
-    end.record(stream)
+    torch.cuda.synchronize()
+    per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n, _ in calls}
+
+    # the timed region: K steps back to back, four eager launches per step with
+    # nothing between them (--graph replays HIP graphs of the same steps
+    # instead; on this stack that measured slower)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.graph:
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K):
+            for _, fn in calls:
+                fn()
+        end.record(stream)
+    else:
+        # one graph holds G consecutive steps; K/G replays run exactly K steps
+        G = max(d for d in range(1, min(K, 10) + 1) if K % d == 0)
+        g = r.capture(G)
+        g.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(K // G):
+            g.replay()
+        end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K
-    per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n, _ in calls}
-    log(f"bench: {ms_step * 1e3:.1f} us/step; per call (us): " +
+    log(f"bench: {ms_step * 1e3:.1f} us/step ({'graph' if args.graph else 'eager'}); per call, eager (us): " +
         ", ".join(f"{n}={v:.1f}" for n, v in per_call_us.items()))
 
     alg_bytes, flops = algorithmic_work(prob)
@@ -203,6 +224,7 @@ def main():
                      "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
                      "mfma_tflops": achieved_tflops, "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
         "per_call_us": per_call_us,
+        "launch": "hip_graph" if args.graph else "eager",
         "step_tflops": flops / (ms_step * 1e-3) / 1e12,
         "step_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
         "cpu_baseline": cpu,

@@ -29,38 +29,33 @@ constexpr int kDC = 512;   // d_c
 constexpr int kNQ = 128;   // absorb_q: columns of q~ per workgroup
 
 // ------------------------------------------------------------------ absorb_q
-// grid (H, d_c / 128); wave w computes columns 32 w .. 32 w + 31 of the quarter
-// for every 32-row tile of M.
+// grid (H, d_c / 128, ceil(M / 64)): workgroup (h, nq, mt) computes columns
+// 128 nq .. 128 nq + 127 of q~ for rows 64 mt .. 64 mt + 63; wave w takes the
+// 32 columns 32 w .. 32 w + 31 of that quarter.  The MFMA computes q~^T =
+// W_UK[h]^T . q_nope^T (A = W_UK^T from the LDS transpose read, B = q_nope
+// rows), so each lane ends up with four consecutive latent columns of one row
+// and stores them as one 8-byte write.
+constexpr int kRowsQ = 64;  // rows of q_nope per workgroup (two 32-row MFMA tiles)
+
 __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           uint16_t* __restrict__ q_cat, int M, int H, int d_r) {
   // W quarter: row k (0..127) holds 16 chunks of 16 B; chunk c sits at c ^ (4 * (k & 3))
   __shared__ __attribute__((aligned(16))) uint8_t wt[kDN * kNQ * 2];
-  const int h = blockIdx.x, nq = blockIdx.y;
+  const int h = blockIdx.x, nq = blockIdx.y, mbase = blockIdx.z * kRowsQ;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const int D = kDC + d_r;
 
-  // A operands (q_nope rows) of the first 32-row tile are requested before the
-  // weight staging so that both memory round trips overlap
-  auto load_a = [&](int m0, uint4* a) {
-    const int m = m0 + (lane & 31);
-    const uint16_t* src = q_nope + ((size_t)min(m, M - 1) * H + h) * kDN + 8 * hi;
+  // every q_nope operand of the workgroup's rows is requested first: both
+  // 32-row tiles, 8 x 16 B per lane each (rows past M read row M - 1)
+  uint4 a[2][kDN / 16];
 #pragma unroll
-    for (int ks = 0; ks < kDN / 16; ++ks) a[ks] = *reinterpret_cast<const uint4*>(src + 16 * ks);
-  };
-  uint4 a_cur[kDN / 16];
-  load_a(0, a_cur);
-
-  // the RoPE part of each row is copied unchanged, 16 B per thread, spread
-  // over the d_c / 128 workgroups of head h (d_r is a multiple of 8)
-  {
-    const int per_row = d_r / 8, nchunk = M * per_row;
-    for (int i = nq * kThreads + tid; i < nchunk; i += kThreads * (kDC / kNQ)) {
-      const int m = i / per_row, k = i - m * per_row;
-      *reinterpret_cast<uint4*>(q_cat + ((size_t)m * H + h) * D + kDC + 8 * k) =
-          *reinterpret_cast<const uint4*>(q_rope + ((size_t)m * H + h) * d_r + 8 * k);
-    }
+  for (int t = 0; t < 2; ++t) {
+    const int m = min(mbase + 32 * t + (lane & 31), M - 1);
+    const uint16_t* src = q_nope + ((size_t)m * H + h) * kDN + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < kDN / 16; ++ks) a[t][ks] = *reinterpret_cast<const uint4*>(src + 16 * ks);
   }
 
   const uint16_t* w = w_uk + (size_t)h * kDN * kDC + nq * kNQ;
@@ -70,6 +65,18 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
     const int q = i * kThreads + tid;
     wv[i] = *reinterpret_cast<const uint4*>(w + (size_t)(q >> 4) * kDC + 8 * (q & 15));
   }
+
+  // the RoPE part of each row is copied unchanged, 16 B per thread, spread
+  // over the d_c / 128 workgroups of the row block (d_r is a multiple of 8)
+  {
+    const int per_row = d_r / 8, rows = min(kRowsQ, M - mbase), nchunk = rows * per_row;
+    for (int i = nq * kThreads + tid; i < nchunk; i += kThreads * (kDC / kNQ)) {
+      const int m = mbase + i / per_row, k = i % per_row;
+      *reinterpret_cast<uint4*>(q_cat + ((size_t)m * H + h) * D + kDC + 8 * k) =
+          *reinterpret_cast<const uint4*>(q_rope + ((size_t)m * H + h) * d_r + 8 * k);
+    }
+  }
+
 #pragma unroll
   for (int i = 0; i < (kDN * kNQ / 8) / kThreads; ++i) {
     const int q = i * kThreads + tid;
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
   const int col = 32 * wave + 16 * (g16 & 1) + 4 * (j16 & 3);
   const int row0 = 8 * (g16 >> 1) + (j16 >> 2);
 
-  bf16x8 bop[kDN / 16];
+  bf16x8 wop[kDN / 16];
 #pragma unroll
   for (int ks = 0; ks < kDN / 16; ++ks) {
     bf16x4 v[2];
@@ -94,129 +101,158 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
       const int off = k * 256 + (((col >> 3) ^ (4 * (k & 3))) * 16) + (col & 7) * 2;
       v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(wt + off));
     }
-    bop[ks] = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    wop[ks] = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
   }
 
-  const int n = nq * kNQ + 32 * wave + (lane & 31);
-  for (int m0 = 0; m0 < M; m0 += 32) {
-    uint4 a_next[kDN / 16];
-    if (m0 + 32 < M) load_a(m0 + 32, a_next);
+  // accumulator element r of lane (row j = lane & 31, hi) is column
+  // 32 wave + 8 (r >> 2) + 4 hi + (r & 3) of the quarter
+  const int c0 = nq * kNQ + 32 * wave + 4 * hi;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int m = mbase + 32 * t + (lane & 31);
+    if (mbase + 32 * t >= M) break;
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kDN / 16; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a_cur[ks]), bop[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[ks], __builtin_bit_cast(bf16x8, a[t][ks]), acc, 0, 0, 0);
+    if (m < M) {
+      uint16_t* dst = q_cat + ((size_t)m * H + h) * D + c0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mr = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (mr < M) q_cat[((size_t)mr * H + h) * D + n] = f32_to_bf16_bits(acc[r]);
-    }
-    if (m0 + 32 < M) {
-#pragma unroll
-      for (int ks = 0; ks < kDN / 16; ++ks) a_cur[ks] = a_next[ks];
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[4 * g]) | ((uint32_t)f32_to_bf16_bits(acc[4 * g + 1]) << 16);
+        const uint32_t up = (uint32_t)f32_to_bf16_bits(acc[4 * g + 2]) | ((uint32_t)f32_to_bf16_bits(acc[4 * g + 3]) << 16);
+        *reinterpret_cast<uint2*>(dst + 8 * g) = make_uint2(lo, up);
+      }
     }
   }
-
 }
 
-// ------------------------------------------------------------------ absorb_out
-// grid (H, ceil(M / 32)); wave w computes outputs 32 w .. 32 w + 31 of d_v.
-__global__ __launch_bounds__(kThreads) void absorb_out_mfma(const float* __restrict__ o,
-                                                            const uint16_t* __restrict__ w_uv,
-                                                            uint16_t* __restrict__ out, int M, int H) {
-  // o tile as bf16 hi and lo: row m (0..31) holds 64 chunks of 16 B; chunk c
-  // sits at c ^ (m & 15)
-  __shared__ __attribute__((aligned(16))) uint8_t ot[2][32 * kDC * 2];
-  const int h = blockIdx.x, m0 = blockIdx.y * 32;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
+// ------------------------------------------------------------ W_UV product
+// u tile (32 rows x 128 outputs) = o tile (32 x 512, LDS bf16 hi + lo, row r's
+// 16-B chunk c at c ^ (r & 15)) . W_UV[h]^T, by 8 waves: wave w computes
+// outputs 32 (w & 3) .. + 31 over d_c half (w >> 2) with the W_UV rows it
+// requested into bw; the second half adds into the first through LDS.  Both
+// kernels that apply W_UV use this, so they round identically.
+constexpr int kThreadsC = 512;
 
-  // every B operand (W_UV rows) of this wave is requested first; its latency
-  // overlaps the staging of o
-  const int v = 32 * wave + (lane & 31);
-  const uint16_t* wrow = w_uv + ((size_t)h * kDV + v) * kDC + 8 * hi;
-  uint4 bw[kDC / 16];
-#pragma unroll
-  for (int ks = 0; ks < kDC / 16; ++ks) bw[ks] = *reinterpret_cast<const uint4*>(wrow + 16 * ks);
+struct WuvOperands {
+  uint4 bw[kDC / 32];
+};
 
+__device__ __forceinline__ void wuv_request(const uint16_t* __restrict__ w_uv, int h, int wave, int lane,
+                                            WuvOperands& op) {
+  const int v = 32 * (wave & 3) + (lane & 31), hi = lane >> 5;
+  const uint16_t* wrow = w_uv + ((size_t)h * kDV + v) * kDC + (wave >> 2) * (kDC / 2) + 8 * hi;
 #pragma unroll
-  for (int i = 0; i < (32 * kDC / 8) / kThreads; ++i) {  // 8 chunks of 8 floats per thread
-    const int q = i * kThreads + tid;
-    const int r = q >> 6, c = q & 63, m = m0 + r;
-    float f[8];
-    if (m < M) {
-      const float4* src = reinterpret_cast<const float4*>(o + ((size_t)m * H + h) * kDC + 8 * c);
-      const float4 x0 = src[0], x1 = src[1];
-      f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
-      f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = 0.f;
-    }
-    uint32_t hw[4], lw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t h0 = f32_to_bf16_bits(f[2 * e]), h1 = f32_to_bf16_bits(f[2 * e + 1]);
-      const uint16_t l0 = f32_to_bf16_bits(f[2 * e] - bf16_bits_to_f32(h0));
-      const uint16_t l1 = f32_to_bf16_bits(f[2 * e + 1] - bf16_bits_to_f32(h1));
-      hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    }
-    const int off = r * 1024 + ((c ^ (r & 15)) * 16);
-    *reinterpret_cast<uint4*>(&ot[0][off]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *reinterpret_cast<uint4*>(&ot[1][off]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-  }
-  __syncthreads();
+  for (int ks = 0; ks < kDC / 32; ++ks) op.bw[ks] = *reinterpret_cast<const uint4*>(wrow + 16 * ks);
+}
 
-  const int r = lane & 31;
+__device__ __forceinline__ void wuv_product(const uint8_t (*ot)[32 * kDC * 2], float (*red)[16][64],
+                                            const WuvOperands& op, int wave, int lane, int m0, int M, int H, int h,
+                                            uint16_t* __restrict__ out) {
+  const int vblk = wave & 3, chalf = wave >> 2, hi = lane >> 5, r = lane & 31;
   f32x16 acc = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < kDC / 16; ++ks) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, bw[ks]);
+  for (int kq = 0; kq < kDC / 32; ++kq) {
+    const int ks = chalf * (kDC / 32) + kq;
+    const bf16x8 b = __builtin_bit_cast(bf16x8, op.bw[kq]);
     const int off = r * 1024 + (((2 * ks + hi) ^ (r & 15)) * 16);
     const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&ot[0][off]);
     const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ot[1][off]);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
   }
+  if (chalf == 1) {
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int m = m0 + 8 * (rr >> 2) + 4 * hi + (rr & 3);
-    if (m < M) out[((size_t)m * H + h) * kDV + v] = f32_to_bf16_bits(acc[rr]);
+    for (int rr = 0; rr < 16; ++rr) red[vblk][rr][lane] = acc[rr];
+  }
+  __syncthreads();
+  if (chalf == 0) {
+    const int v = 32 * vblk + r;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const float x = acc[rr] + red[vblk][rr][lane];
+      const int m = m0 + 8 * (rr >> 2) + 4 * hi + (rr & 3);
+      if (m < M) out[((size_t)m * H + h) * kDV + v] = f32_to_bf16_bits(x);
+    }
   }
 }
 
+// o row r (fp32, 8 consecutive values starting at column 8 c + 4 half) into
+// the hi/lo tile: writes the 8-byte half 'half' of 16-B chunk c
+__device__ __forceinline__ void stage_hilo(uint8_t (*ot)[32 * kDC * 2], int r, int c, int half, const float4& x) {
+  const float e[4] = {x.x, x.y, x.z, x.w};
+  uint32_t hw[2], lw[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint16_t h0 = f32_to_bf16_bits(e[2 * q]), h1 = f32_to_bf16_bits(e[2 * q + 1]);
+    const uint16_t l0 = f32_to_bf16_bits(e[2 * q] - bf16_bits_to_f32(h0));
+    const uint16_t l1 = f32_to_bf16_bits(e[2 * q + 1] - bf16_bits_to_f32(h1));
+    hw[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lw[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  const int off = r * 1024 + ((c ^ (r & 15)) * 16) + 8 * half;
+  *reinterpret_cast<uint2*>(&ot[0][off]) = make_uint2(hw[0], hw[1]);
+  *reinterpret_cast<uint2*>(&ot[1][off]) = make_uint2(lw[0], lw[1]);
+}
+
+// ------------------------------------------------------------------ absorb_out
+// grid (H, ceil(M / 32)), 8 waves: the o tile is staged as bf16 hi + lo, then
+// multiplied by W_UV[h] (requested first, so its latency overlaps the staging).
+__global__ __launch_bounds__(kThreadsC) void absorb_out_mfma(const float* __restrict__ o,
+                                                             const uint16_t* __restrict__ w_uv,
+                                                             uint16_t* __restrict__ out, int M, int H) {
+  __shared__ __attribute__((aligned(16))) uint8_t ot[2][32 * kDC * 2];
+  __shared__ __attribute__((aligned(16))) float red[4][16][64];
+  const int h = blockIdx.x, m0 = blockIdx.y * 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  WuvOperands op;
+  wuv_request(w_uv, h, wave, lane, op);
+  // thread (row r, lane j of 16) stages float4 columns j + 16 k, k < 8
+  {
+    const int r = tid >> 4, j = tid & 15, m = m0 + r;
+    float4 x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      x[k] = (m < M) ? reinterpret_cast<const float4*>(o + ((size_t)m * H + h) * kDC)[j + 16 * k]
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) stage_hilo(ot, r, (j + 16 * k) >> 1, (j + 16 * k) & 1, x[k]);
+  }
+  __syncthreads();
+  wuv_product(ot, red, op, wave, lane, m0, M, H, h, out);
+}
 
 // ------------------------------------------------------------ combine + absorb_out
 // The log-sum-exp merge of the split partials fused with the W_UV product, so
 // that the merged latent output never leaves the chip:
 //   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s,  u = W_UV[h] o.
-// grid (H, ceil(M / 32)); the 32 rows of a workgroup are merged straight into
-// the bf16 hi/lo LDS tile of absorb_out_mfma.  Splits with lse_s = -inf are
-// skipped (their o_s is never read).  o_latent and lse are written when given.
+// grid (H, ceil(M / 32)), 8 waves.  The 32 rows of a workgroup are merged
+// straight into the bf16 hi/lo LDS tile of absorb_out_mfma; each thread owns
+// 32 columns of one row and keeps two splits' loads in flight.  Splits with
+// lse_s = -inf are skipped (their o_s is never read).  o_latent and lse are
+// written when given.
 constexpr int kMaxFusedSplits = 64;
 
-__global__ __launch_bounds__(kThreads) void combine_out_mfma(const float* __restrict__ o_part,
-                                                             const float* __restrict__ lse_part,
-                                                             const uint16_t* __restrict__ w_uv,
-                                                             uint16_t* __restrict__ out, float* __restrict__ o_latent,
-                                                             float* __restrict__ lse_out, int M, int H, int S) {
+__global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const float* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ out, float* __restrict__ o_latent,
+                                                              float* __restrict__ lse_out, int M, int H, int S) {
   __shared__ __attribute__((aligned(16))) uint8_t ot[2][32 * kDC * 2];
   __shared__ float wts[32][kMaxFusedSplits];
+  __shared__ __attribute__((aligned(16))) float red[4][16][64];
   const int h = blockIdx.x, m0 = blockIdx.y * 32;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  WuvOperands op;
+  wuv_request(w_uv, h, wave, lane, op);
 
-  // every B operand (W_UV rows) of this wave is requested first
-  const int v = 32 * wave + (lane & 31);
-  const uint16_t* wrow = w_uv + ((size_t)h * kDV + v) * kDC + 8 * hi;
-  uint4 bw[kDC / 16];
-#pragma unroll
-  for (int ks = 0; ks < kDC / 16; ++ks) bw[ks] = *reinterpret_cast<const uint4*>(wrow + 16 * ks);
-
-  // split weights: 8 lanes per row
+  // split weights: 16 lanes per row (two groups of 8 compute the same total)
   {
-    const int r = tid >> 3, j = tid & 7, m = m0 + r;
+    const int r = tid >> 4, j = tid & 15, m = m0 + r;
     const float* lp = lse_part + ((size_t)min(m, M - 1) * H + h) * S;
-    const float total = split_lse(lp, S, j);
-    for (int s2 = j; s2 < S; s2 += 8) {
+    const float total = split_lse(lp, S, j & 7);
+    for (int s2 = j; s2 < S; s2 += 16) {
       const float ls = lp[s2];
       wts[r][s2] = (ls == -INFINITY || m >= M) ? 0.f : expf(ls - total);
     }
@@ -224,71 +260,49 @@ __global__ __launch_bounds__(kThreads) void combine_out_mfma(const float* __rest
   }
   __syncthreads();
 
-  // merge: thread (row r, lane j of 8) owns float4 columns j + 8 k, k < 16
+  // merge: thread (row r, lane j of 16) owns float4 columns j + 16 k, k < 8
   {
-    const int r = tid >> 3, j = tid & 7, m = m0 + r;
-    float4 acc[16];
+    const int r = tid >> 4, j = tid & 15, m = m0 + r;
+    float4 acc[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < 8; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (m < M) {
-      const float4* src = reinterpret_cast<const float4*>(o_part + ((size_t)m * H + h) * S * kDC);
-      for (int s2 = 0; s2 < S; ++s2) {
-        const float wgt = wts[r][s2];
-        if (wgt == 0.f) continue;
-        float4 x[16];
+      const float4* src = reinterpret_cast<const float4*>(o_part + ((size_t)m * H + h) * S * kDC) + j;
+      auto fma4 = [&](float wgt, const float4* x) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) x[k] = src[(size_t)s2 * (kDC / 4) + j + 8 * k];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < 8; ++k) {
           acc[k].x = fmaf(wgt, x[k].x, acc[k].x);
           acc[k].y = fmaf(wgt, x[k].y, acc[k].y);
           acc[k].z = fmaf(wgt, x[k].z, acc[k].z);
           acc[k].w = fmaf(wgt, x[k].w, acc[k].w);
         }
+      };
+      for (int s2 = 0; s2 < S; s2 += 2) {
+        const float w0 = wts[r][s2];
+        const float w1 = (s2 + 1 < S) ? wts[r][s2 + 1] : 0.f;
+        float4 x0[8], x1[8];
+        if (w0 != 0.f) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x0[k] = src[(size_t)s2 * (kDC / 4) + 16 * k];
+        }
+        if (w1 != 0.f) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x1[k] = src[(size_t)(s2 + 1) * (kDC / 4) + 16 * k];
+        }
+        if (w0 != 0.f) fma4(w0, x0);
+        if (w1 != 0.f) fma4(w1, x1);
       }
       if (o_latent != nullptr) {
-        float4* dst = reinterpret_cast<float4*>(o_latent + ((size_t)m * H + h) * kDC);
+        float4* dst = reinterpret_cast<float4*>(o_latent + ((size_t)m * H + h) * kDC) + j;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) dst[j + 8 * k] = acc[k];
+        for (int k = 0; k < 8; ++k) dst[16 * k] = acc[k];
       }
     }
-    // float4 column f = j + 8 k covers half of 16-B chunk c = f / 2 (8 bytes of bf16)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int f = j + 8 * k, c = f >> 1;
-      const float e[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
-      uint32_t hw[2], lw[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint16_t h0 = f32_to_bf16_bits(e[2 * q]), h1 = f32_to_bf16_bits(e[2 * q + 1]);
-        const uint16_t l0 = f32_to_bf16_bits(e[2 * q] - bf16_bits_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16_bits(e[2 * q + 1] - bf16_bits_to_f32(h1));
-        hw[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lw[q] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
-      const int off = r * 1024 + ((c ^ (r & 15)) * 16) + 8 * (f & 1);
-      *reinterpret_cast<uint2*>(&ot[0][off]) = make_uint2(hw[0], hw[1]);
-      *reinterpret_cast<uint2*>(&ot[1][off]) = make_uint2(lw[0], lw[1]);
-    }
+    for (int k = 0; k < 8; ++k) stage_hilo(ot, r, (j + 16 * k) >> 1, (j + 16 * k) & 1, acc[k]);
   }
   __syncthreads();
-
-  const int r = lane & 31;
-  f32x16 acc = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < kDC / 16; ++ks) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, bw[ks]);
-    const int off = r * 1024 + (((2 * ks + hi) ^ (r & 15)) * 16);
-    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&ot[0][off]);
-    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&ot[1][off]);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
-  }
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int m = m0 + 8 * (rr >> 2) + 4 * hi + (rr & 3);
-    if (m < M) out[((size_t)m * H + h) * kDV + v] = f32_to_bf16_bits(acc[rr]);
-  }
+  wuv_product(ot, red, op, wave, lane, m0, M, H, h, out);
 }
 
 }  // namespace
@@ -300,7 +314,7 @@ bool absorb_mfma_supported(const mla_dims& d) {
 hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
                                 void* q_cat, hipStream_t stream) {
   const int M = d.batch * d.q_len;
-  hipLaunchKernelGGL(absorb_q_mfma, dim3(d.num_heads, kDC / kNQ), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(absorb_q_mfma, dim3(d.num_heads, kDC / kNQ, (M + kRowsQ - 1) / kRowsQ), dim3(kThreads), 0, stream,
                      (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, (uint16_t*)q_cat, M,
                      d.num_heads, d.d_rope);
   return hipGetLastError();
@@ -311,7 +325,7 @@ int combine_out_max_splits() { return kMaxFusedSplits; }
 hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o_part, const float* lse_part,
                                    const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream) {
   const int M = d.batch * d.q_len;
-  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreads), 0, stream, o_part, lse_part,
+  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreadsC), 0, stream, o_part, lse_part,
                      (const uint16_t*)w_uv, (uint16_t*)out, o_latent, lse, M, d.num_heads, splits);
   return hipGetLastError();
 }
@@ -319,7 +333,7 @@ hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o
 hipError_t launch_absorb_out_mfma(const mla_dims& d, const float* o, const void* w_uv, void* out,
                                   hipStream_t stream) {
   const int M = d.batch * d.q_len;
-  hipLaunchKernelGGL(absorb_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreads), 0, stream, o,
+  hipLaunchKernelGGL(absorb_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreadsC), 0, stream, o,
                      (const uint16_t*)w_uv, (uint16_t*)out, M, d.num_heads);
   return hipGetLastError();
 }

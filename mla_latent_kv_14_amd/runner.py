@@ -74,6 +74,30 @@ class DecodeRunner:
                                       self.o if (keep_latent or not fused) else None,
                                       self.lse if (keep_latent or not fused) else None, stream)
 
+    def fused_step(self, stream=None):
+        """One decode step as the bench runs it: plan, absorb_q, attention, fused merge + W_UV."""
+        self.plan(stream)
+        self.absorb_q(stream)
+        self.decode_planned(stream)
+        self.combine_absorb_out(stream=stream)
+
+    def capture(self, steps=1):
+        """Record `steps` consecutive fused_steps into one HIP graph
+        (torch.cuda.CUDAGraph) and return it.
+
+        The libmla calls enqueue kernels only (no memsets, no allocation), so
+        the graph holds exactly the four kernels of each step."""
+        side = torch.cuda.Stream(device=self.device)
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(side):
+            self.fused_step()  # warm-up on the capture stream
+        torch.cuda.current_stream(self.device).wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                self.fused_step()
+        return g
+
     def step(self, stream=None):
         """One full decode step: absorb_q -> decode -> combine -> absorb_out."""
         self.absorb_q(stream)

@@ -196,6 +196,35 @@ def test_combine_absorb_out_keeps_latent(name, lens):
     assert torch.equal(r.o, o1) and torch.equal(r.lse, l1) and torch.equal(r.u, u1)
 
 
+def test_graph_replay_matches_eager():
+    """The step captured in a HIP graph replays to the eager result, with eager work and input changes between replays."""
+    wl = workload("single_4k_bf16", batch=3, lengths=("fixed", (700, 129, 1500)))
+    p = make_problem(wl, 61)
+    r = DecodeRunner(p)
+    r.fused_step()
+    torch.cuda.synchronize()
+    u_ref = r.u.clone()
+    g = r.capture()
+    torch.cuda.synchronize()
+    for k in range(3):
+        r.u.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(r.u, u_ref), f"replay {k} differs from the eager step"
+        _ = (torch.arange(4096, device=r.u.device, dtype=torch.float32) * k).sum().item()  # eager work between replays
+    # new inputs in place: the graph reads them at replay
+    r.q_nope.mul_(-1)
+    r.fused_step()
+    torch.cuda.synchronize()
+    u2 = r.u.clone()
+    assert not torch.equal(u2, u_ref)
+    r.u.fill_(0)
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(r.u, u2)
+
+
 def test_combine_against_oracle():
     wl = workload("single_4k_bf16", batch=2, heads=4, lengths=("fixed", (5, 6)))
     p = make_problem(wl, 43)
