@@ -136,6 +136,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   constexpr int CG = 4 / RG;   // waves sharing one group of 32 rows (split over O columns)
   constexpr int MB = 16 / CG;  // 32-column blocks of O per wave
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kSubBytes];
+  // sink for the copies issued when there is no sub-tile left to fetch (so
+  // that the score loop carries no per-step condition); never read
+  __shared__ __attribute__((aligned(1024))) uint8_t sink[kThreads / 64 * 1024];
   __shared__ int red_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -156,8 +159,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   walk.init(ws, w);
   if (w >= walk.groups) return;
 
-  // Per-lane LDS byte offsets inside a sub-tile, recomputed per sub-tile from
-  // the lane index (a few integer ops) instead of being held in registers:
+  // Per-lane LDS byte offsets inside a sub-tile (held in registers):
   //   score operand v (logical chunk 2 v + hi of row r = lane & 31):
   //     r * 1152 + 16 ((2 v + hi) ^ g(r))
   //   transpose operand (h, mb parity par): this lane supplies row
@@ -165,28 +167,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   //     sw = g(tr_row) ^ (h << 1) the swizzled chunk is
   //     4 (mb ^ (sw >> 2)) + (y ^ (sw & 3)), y = tr_col >> 3, and the mb ^ bit
   //     swap is folded into one base per (h, mb parity).
-  // (the empty asm hides that the lane index is loop-invariant, so that the
-  // compiler recomputes rather than hoists and holds these values)
-  auto opaque_lane = [&]() {
-    int l = lane;
-    __asm__ volatile("" : "+v"(l));
-    return l;
-  };
-  auto kbase = [&](int v) {
-    const int ln = opaque_lane();
-    const int r = ln & 31;
-    return r * kRowBytes + 16 * ((2 * v + (ln >> 5)) ^ swz(r));
-  };
-  auto vbase = [&](int h, int par) {
-    const int ln = opaque_lane();
-    const int g16 = ln >> 4, j16 = ln & 15;
+  int kbase_r[4];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) kbase_r[v] = r * kRowBytes + 16 * ((2 * v + hi) ^ swz(r));
+  }
+  int vbase_r[2][2];
+  {
+    const int g16 = lane >> 4, j16 = lane & 15;
     const int tr_row = 4 * (g16 >> 1) + (j16 >> 2);
     const int y = 2 * (g16 & 1) + ((j16 & 3) >> 1);
     const int s2 = (swz(tr_row) >> 2) & 1;
-    const int sw = swz(tr_row) ^ (h << 1);
-    const int b0 = tr_row * kRowBytes + 16 * (y ^ (sw & 3)) + 8 * (j16 & 1) + 64 * (cg * MB);
-    return b0 + (s2 ? (par ? -64 : 64) : 0);
-  };
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sw = swz(tr_row) ^ (h << 1);
+      const int b0 = tr_row * kRowBytes + 16 * (y ^ (sw & 3)) + 8 * (j16 & 1) + 64 * (cg * MB);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) vbase_r[h][par] = b0 + (s2 ? (par ? -64 : 64) : 0);
+    }
+  }
+  auto kbase = [&](int v) { return kbase_r[v]; };
+  auto vbase = [&](int h, int par) { return vbase_r[h][par]; };
   // Source offset inside a sub-tile of this lane's part of copy piece i:
   // the piece fills physical chunk q = 64 (wave + 4 i) + lane, which holds
   // logical chunk (q mod 72) ^ g(r) of row r = q / 72.  Recomputed per copy
@@ -230,11 +232,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       blk = min(max(blk, 0), a.num_blocks - 1);
       return cache + ((size_t)blk * a.block_size + (t % a.block_size)) * kRowBytes;
     };
-    auto dma = [&](const uint8_t* base, int sub, int i) {
-      const uint32_t dst = (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes + wave * 1024;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + 4096 * i);
+    auto dma_to = [&](const uint8_t* base, uint32_t dst, uint32_t stride, int i) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + stride * i);
       __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_src(i)), "s"(base), "{m0}"(m0)
                        : "memory");
+    };
+    auto dma = [&](const uint8_t* base, int sub, int i) {
+      dma_to(base, (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes + wave * 1024, 4096, i);
     };
     auto issue = [&](int sub) {
       const uint8_t* base = tile_src(sub);
@@ -329,9 +333,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         }
         // Sub-tile i+3 is copied during the score loop below, one 1 KiB piece
         // every fourth MFMA: a wave can queue only a few copies, and a burst of
-        // nine would stall it for their whole transfer.
-        const int copy_on = (i + 3 < n_sub) ? 1 : 0;
-        const uint8_t* copy_src = copy_on ? tile_src(i + 3) : cache;
+        // nine would stall it for their whole transfer.  Every copy is
+        // counted by the waits below (vmcnt), the sink's ones included.
+        // with no sub-tile i+3 the copies re-read the last sub-tile (in L2)
+        // into the sink, so every step of the loop issues the same code
+        const bool copy_on = i + 3 < n_sub;
+        const uint8_t* copy_src = tile_src(copy_on ? i + 3 : n_sub - 1);
+        const uint32_t copy_dst = copy_on ? (uint32_t)(uintptr_t)smem + ((i + 3) & (kStages - 1)) * kSubBytes + wave * 1024
+                                          : (uint32_t)(uintptr_t)sink + wave * 1024;
+        const uint32_t copy_stride = copy_on ? 4096u : 0u;
 
         // masking of sub-tile i (rare: only where some row's last visible token falls inside)
         if (t0 + kSub > lim_all) {
@@ -382,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
             if (ks == 0) mfma_v0(sn, kop[0], q[0]);
             else mfma_v(sn, kop[ks % kAhead], q[ks]);
             if (ks < kPieces) piece(ks);
-            if (ks % 4 == 2 && copy_on > 0) dma(copy_src, i + 3, ks / 4);
+            if (ks % 4 == 2) dma_to(copy_src, copy_dst, copy_stride, ks / 4);
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
