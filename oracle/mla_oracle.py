@@ -47,6 +47,9 @@ __all__ = [
     "latent_attention_partial_reference",
     "cache_elements_per_token",
     "cache_bytes",
+    "rope_reference",
+    "cache_rows_reference",
+    "cache_append_reference",
 ]
 
 
@@ -223,3 +226,68 @@ def cache_elements_per_token(kind: str, *, n_h=128, d_h=128, d_c=512, d_rope=64,
 def cache_bytes(kind: str, tokens: int, bytes_per_element: int, layers: int = 1, **dims) -> int:
     """Bytes of cache for ``tokens`` tokens over ``layers`` layers."""
     return cache_elements_per_token(kind, **dims) * tokens * bytes_per_element * layers
+
+
+def rope_reference(x, pos, base=10000.0):
+    """Rotary position embedding of the last axis of x at integer positions pos.
+
+    "Deconstructing DeepSeek V4 Pro ..." -- the apply_rope helper of its MLA
+    module: element pairs (x[2p], x[2p+1]) are rotated by the angle
+    theta_p = pos / base^(2p / d) with d the width of the last axis:
+        out[2p]   = x[2p] cos(theta_p) - x[2p+1] sin(theta_p)
+        out[2p+1] = x[2p+1] cos(theta_p) + x[2p] sin(theta_p)
+    x has shape [..., d] and pos broadcasts against x[..., 0].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE needs an even width")
+    pos = np.asarray(pos, dtype=np.float64)[..., None]  # [..., 1]
+    p = np.arange(d // 2, dtype=np.float64)
+    theta = pos / np.power(float(base), 2.0 * p / d)  # [..., d/2]
+    c, s_ = np.cos(theta), np.sin(theta)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s_
+    out[..., 1::2] = x1 * c + x0 * s_
+    return out
+
+
+def cache_rows_reference(h, w_dkv, w_kr, pos, base=10000.0):
+    """Cache rows [c^KV | k^R] of hidden states h at positions pos.
+
+    c^KV_t = W^DKV h_t and k^R_t = RoPE_t(W^KR h_t): "DeepSeek-V3 MLA:
+    Multi-Head Latent Attention Guide", Core Architecture section 1 (joint KV
+    compression) and section 3 (decoupled RoPE key); the weights are Linear
+    weights, W^DKV in R^{d_c x d} and W^KR in R^{d_rope x d} (the V4 Pro
+    module's W_dkv and W_kr).  h has shape [..., d]; returns [..., d_c + d_rope].
+    """
+    h = np.asarray(h, dtype=np.float64)
+    c = h @ np.asarray(w_dkv, dtype=np.float64).T
+    k = rope_reference(h @ np.asarray(w_kr, dtype=np.float64).T, pos, base)
+    return np.concatenate([c, k], axis=-1)
+
+
+def cache_append_reference(cache, block_table, seq_lens, h, w_dkv, w_kr, base=10000.0):
+    """The paged cache after writing the rows of the q_len new tokens.
+
+    Sequence b holds seq_lens[b] tokens including its q_len new ones (the
+    Guide's decode step appends the new latent before scoring); new token j
+    sits at position t = seq_lens[b] - q_len + j, in physical block
+    block_table[b, t // bs] at slot t % bs, and its row is
+    cache_rows_reference(h[b, j], ..., pos=t).  Every other slot is left as
+    it was.  Returns a float64 copy of the cache.
+    """
+    out = np.array(cache, dtype=np.float64, copy=True)
+    h = np.asarray(h, dtype=np.float64)
+    B, Lq, _ = h.shape
+    bs = out.shape[1]
+    for b in range(B):
+        for j in range(Lq):
+            t = int(seq_lens[b]) - Lq + j
+            if t < 0:
+                raise ValueError("a sequence is shorter than q_len")
+            row = cache_rows_reference(h[b, j], w_dkv, w_kr, t, base)
+            out[int(block_table[b, t // bs]), t % bs, :] = row
+    return out
+

@@ -14,7 +14,11 @@ Independent routes used here:
   * pure-Python scalar loops on tiny inputs;
   * closed forms (length-1 context, zero query, constant latent rows);
   * invariances (physical block permutation, causal reduction for q_len = 2);
-  * the log-sum-exp merge identity over a split of the keys.
+  * the log-sum-exp merge identity over a split of the keys;
+  * for the cache append: RoPE as multiplication by a unit complex number
+    (numpy complex arithmetic, angle from logarithms), RoPE's defining
+    relative-position property, 2 x 2 rotation matrices in scalar loops, and
+    the paging invariant that only the new tokens' slots change.
 """
 from __future__ import annotations
 
@@ -269,6 +273,86 @@ def pin_select(orc, seed=11):
     assert np.isnan(us[0, :, 1]).all()
 
 
+def pin_rope_complex(orc, seed=12):
+    """RoPE of pair p is multiplication of x[2p] + i x[2p+1] by exp(i pos base^(-2p/d))."""
+    rng = np.random.default_rng(seed)
+    d, base = 16, 10000.0
+    x = rng.standard_normal((5, d))
+    pos = np.array([0, 1, 7, 1000, 131071])
+    z = x[:, 0::2] + 1j * x[:, 1::2]
+    p = np.arange(d // 2)
+    ang = pos[:, None] * np.exp(-(2.0 * p / d) * math.log(base))
+    zr = z * np.exp(1j * ang)
+    want = np.empty_like(x)
+    want[:, 0::2], want[:, 1::2] = zr.real, zr.imag
+    _close(orc.rope_reference(x, pos, base), want, rtol=1e-9, atol=1e-9)
+
+
+def pin_rope_relative(orc, seed=13):
+    """<RoPE_m(q), RoPE_n(k)> = <RoPE_{m-n}(q), k>; norms of pairs are kept; position 0 is the identity."""
+    rng = np.random.default_rng(seed)
+    d = 8
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for m, n in [(5, 2), (17, 17), (3, 40)]:
+        lhs = orc.rope_reference(q, m) @ orc.rope_reference(k, n)
+        rhs = orc.rope_reference(q, m - n) @ k
+        assert abs(lhs - rhs) <= 1e-10 * (1 + abs(rhs))
+    r = orc.rope_reference(q, 123)
+    _close(r[0::2] ** 2 + r[1::2] ** 2, q[0::2] ** 2 + q[1::2] ** 2)
+    assert np.array_equal(orc.rope_reference(q, 0), q)
+
+
+def pin_cache_rows_bruteforce(orc, seed=14):
+    """Cache rows from scalar loops: c_n = sum_k W^DKV[n, k] h[k], k^R from explicit 2 x 2 rotations."""
+    rng = np.random.default_rng(seed)
+    d, d_c, d_r = 6, 5, 4
+    h = rng.standard_normal(d)
+    w_dkv, w_kr = rng.standard_normal((d_c, d)), rng.standard_normal((d_r, d))
+    pos = 9
+    want = []
+    for n in range(d_c):
+        want.append(sum(float(w_dkv[n, k]) * float(h[k]) for k in range(d)))
+    kr = [sum(float(w_kr[n, k]) * float(h[k]) for k in range(d)) for n in range(d_r)]
+    for pp in range(d_r // 2):
+        th = pos / (10000.0 ** (2.0 * pp / d_r))
+        rot = [[math.cos(th), -math.sin(th)], [math.sin(th), math.cos(th)]]
+        a, b = kr[2 * pp], kr[2 * pp + 1]
+        want += [rot[0][0] * a + rot[0][1] * b, rot[1][0] * a + rot[1][1] * b]
+    _close(orc.cache_rows_reference(h, w_dkv, w_kr, pos), np.array(want))
+
+
+def pin_cache_append(orc, seed=15):
+    """Appending writes exactly the q_len new tokens' slots (through the table), nothing else; the
+    decode over the appended cache equals the decode over contiguous rows with the new rows put last."""
+    p = Tiny(seed, B=2, Lq=2, lens=(5, 11))
+    rng = np.random.default_rng(seed + 100)
+    d = 7
+    h = rng.standard_normal((p.B, p.Lq, d))
+    w_dkv, w_kr = rng.standard_normal((p.d_c, d)), rng.standard_normal((p.d_r, d))
+    new = orc.cache_append_reference(p.cache, p.table, p.lens, h, w_dkv, w_kr)
+    touched = np.zeros(p.cache.shape[:2], dtype=bool)
+    for b in range(p.B):
+        for j in range(p.Lq):
+            t = int(p.lens[b]) - p.Lq + j
+            touched[p.table[b, t // p.bs], t % p.bs] = True
+            p.rows[b][t] = orc.cache_rows_reference(h[b, j], w_dkv, w_kr, t)
+    same = ~touched
+    assert np.array_equal(np.isnan(new[same]), np.isnan(p.cache[same]))
+    assert np.array_equal(np.nan_to_num(new[same]), np.nan_to_num(p.cache[same]))
+    p.cache = new
+    u, o, lse = p.run(orc)
+    # the absorbed algebra on the contiguous rows (which now hold the new rows)
+    for b in range(p.B):
+        L = int(p.lens[b])
+        for j in range(p.Lq):
+            rows = p.rows[b][: L - p.Lq + j + 1]
+            for hh in range(p.H):
+                qc = p.w_uk[hh].T @ p.q_nope[b, j, hh]
+                s = p.scale * (rows[:, : p.d_c] @ qc + rows[:, p.d_c:] @ p.q_rope[b, j, hh])
+                e = np.exp(s - s.max())
+                _close(o[b, j, hh], (e / e.sum()) @ rows[:, : p.d_c])
+
+
 ALL_PINS = [
     pin_absorbed_route,
     pin_library_sdpa,
@@ -282,4 +366,8 @@ ALL_PINS = [
     pin_absorb_q,
     pin_absorb_out,
     pin_select,
+    pin_rope_complex,
+    pin_rope_relative,
+    pin_cache_rows_bruteforce,
+    pin_cache_append,
 ]

@@ -90,6 +90,14 @@ MUTATIONS = {
     "absorb_out_transposed": ("u[:, :, h, :] = o[:, :, h, :] @ w_uv[h].T",
                               "u[:, :, h, :] = (w_uv[h] @ o[:, :, h, :].reshape(-1, o.shape[3]).T).T.reshape(u[:, :, h, :].shape)[..., ::-1]"),
     "partial_scale_dropped": ("s = scale * (rows[idx] @ q_cat[r])", "s = rows[idx] @ q_cat[r]"),
+    "rope_sign_flipped": ("out[..., 0::2] = x0 * c - x1 * s_", "out[..., 0::2] = x0 * c + x1 * s_"),
+    "rope_half_split_pairs": ("x0, x1 = x[..., 0::2], x[..., 1::2]", "x0, x1 = x[..., : d // 2], x[..., d // 2:]"),
+    "rope_exponent_wrong": ("theta = pos / np.power(float(base), 2.0 * p / d)", "theta = pos / np.power(float(base), p / d)"),
+    "append_position_off_by_one": ("t = int(seq_lens[b]) - Lq + j\n", "t = int(seq_lens[b]) - Lq + j + 1\n"),
+    "append_rope_dropped": ("k = rope_reference(h @ np.asarray(w_kr, dtype=np.float64).T, pos, base)",
+                            "k = h @ np.asarray(w_kr, dtype=np.float64).T"),
+    "append_wdkv_transposed": ("c = h @ np.asarray(w_dkv, dtype=np.float64).T",
+                               "c = (np.asarray(w_dkv, dtype=np.float64) @ np.resize(h, np.asarray(w_dkv).shape[1]))[..., : np.asarray(w_dkv).shape[0]] * 0 + h[..., : np.asarray(w_dkv).shape[0]]"),
 }
 
 
