@@ -56,6 +56,18 @@ def algorithmic_work(prob):
     return rows_bytes + q_bytes + table_bytes + o_bytes, flops
 
 
+def append_work(prob, d_model):
+    """Bytes and flops of one cache append: the two projection weights, the
+    hidden states, the written rows and the table entries and lengths read;
+    2 * d_model flops per written element."""
+    wl = prob.wl
+    esz = 4 if wl.dtype == "f32" else 2
+    D = wl.d_c + wl.d_rope
+    M = wl.batch * wl.q_len
+    nbytes = (D * d_model + M * d_model + M * D) * esz + M * 4 + wl.batch * 4
+    return nbytes, 2 * M * D * d_model
+
+
 def source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -130,7 +142,7 @@ def main():
 
     import torch
 
-    from mla_latent_kv_14_amd.inputs import make_problem, workload
+    from mla_latent_kv_14_amd.inputs import make_append_inputs, make_problem, workload
     from mla_latent_kv_14_amd.runner import DecodeRunner
 
     if not torch.cuda.is_available():
@@ -190,6 +202,23 @@ def main():
     log(f"bench: {ms_step * 1e3:.1f} us/step ({'graph' if args.graph else 'eager'}); per call, eager (us): " +
         ", ".join(f"{n}={v:.1f}" for n, v in per_call_us.items()))
 
+    # the cache append (the step just before attention in a decode loop),
+    # timed on its own: K back-to-back calls; it rewrites the same slots
+    app = make_append_inputs(prob)
+    r.setup_append(app)
+    for _ in range(args.warmup):
+        r.cache_append()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a0.record(stream)
+    for i in range(K):
+        r.cache_append()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    append_us = 1e3 * a0.elapsed_time(a1) / K
+    ap_bytes, ap_flops = append_work(prob, app.d_model)
+    log(f"bench: cache append {append_us:.1f} us/call (d_model={app.d_model})")
+
     alg_bytes, flops = algorithmic_work(prob)
     dec_s = per_call_us["decode"] * 1e-6
     achieved_gbs = alg_bytes / dec_s / 1e9
@@ -228,6 +257,10 @@ def main():
         "step_tflops": flops / (ms_step * 1e-3) / 1e12,
         "step_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
         "cpu_baseline": cpu,
+        "cache_append": {"us_per_call": append_us, "d_model": app.d_model, "alg_bytes": ap_bytes,
+                         "gbs": ap_bytes / (append_us * 1e-6) / 1e9,
+                         "hbm_frac": ap_bytes / (append_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "tflops": ap_flops / (append_us * 1e-6) / 1e12},
     }
     print(json.dumps(rec), flush=True)
 

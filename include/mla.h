@@ -182,6 +182,42 @@ int mla_combine_absorb_out(const mla_dims* dims, int32_t num_splits, const float
  * splits), else 0 (also for invalid arguments).  Host only. */
 int mla_combine_absorb_out_fused(const mla_dims* dims, int32_t num_splits);
 
+/* ---- cache append: the step just before attention ---------------------- */
+
+/* Bytes of device workspace mla_cache_append needs for these dims and model
+ * width d_model (0 when the portable kernel serves them; the workspace may
+ * then be NULL).  Host only; MLA_ERR_INVALID_ARG for d_model outside
+ * [1, 65536] or a NULL bytes. */
+int mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t d_model, size_t* bytes);
+
+/* Write the cache rows of the q_len new tokens of every sequence
+ * ("DeepSeek-V3 MLA: Multi-Head Latent Attention Guide", Core Architecture
+ * section 1, joint KV compression, and section 3, decoupled RoPE key):
+ *   c_t   = W^DKV h_t                          (d_c values)
+ *   k^R_t = RoPE_t(W^KR h_t)                   (d_rope values)
+ *   kv_cache[block_table[b, t / bs], t % bs, :] = [c_t | k^R_t]
+ * for token j of sequence b at position t = seq_lens[b] - q_len + j (the
+ * lengths count the new tokens, as mla_decode expects).  RoPE rotates each
+ * pair (x[2p], x[2p+1]) by theta_p = t / rope_base^(2p / d_rope), as the
+ * apply_rope helper of the MLA module in "Deconstructing DeepSeek V4 Pro"
+ * does; rope_base is 10000 there.
+ *   h       [B,Lq,d_model]  hidden states of the new tokens, storage type
+ *   w_dkv   [d_c,d_model]   W^DKV (a Linear weight), storage type
+ *   w_kr    [d_rope,d_model] W^KR, storage type (may be NULL if d_rope = 0)
+ *   kv_cache [num_blocks,block_size,d_c+d_rope] storage type, updated in place
+ *   workspace  at least mla_cache_append_workspace_bytes() bytes, contents
+ *              on entry irrelevant (float32 split-K partials)
+ * Products accumulate in float32; the RoPE angle, its sine and cosine and
+ * the rotation are evaluated in float64; each value is rounded once to the
+ * storage type.  Only the slots of the new tokens are written.  A token whose
+ * position falls outside [0, max_blocks_per_seq * block_size) or whose block
+ * id falls outside [0, num_blocks) is skipped.  How d_model is split, and
+ * so the order of the float32 additions, follows the device's compute-unit
+ * count: the result is reproducible on one device type. */
+int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                     float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* mla_status_str(int status);
 

@@ -62,6 +62,8 @@ def load() -> ctypes.CDLL:
         "mla_absorb_out": [D, P, P, P, P],
         "mla_combine_absorb_out": [D, I32, P, P, P, P, P, P, P],
         "mla_combine_absorb_out_fused": [D, I32],
+        "mla_cache_append_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
+        "mla_cache_append": [D, I32, P, P, P, F32, P, P, P, P, SZ, P],
         "mla_version": [],
     }
     for name, args in sig.items():
@@ -221,3 +223,27 @@ def mla_combine_absorb_out(dims, num_splits, o_partial, lse_partial, w_uv, out, 
 def mla_combine_absorb_out_fused(dims, num_splits) -> bool:
     return bool(load().mla_combine_absorb_out_fused(ctypes.byref(dims), int(num_splits)))
 
+
+
+def mla_cache_append_workspace_bytes(dims, d_model: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_cache_append_workspace_bytes",
+           load().mla_cache_append_workspace_bytes(ctypes.byref(dims), int(d_model), ctypes.byref(out)))
+    return out.value
+
+
+def mla_cache_append(dims, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens, kv_cache, workspace=None,
+                     stream=None):
+    d, st = dims, _storage_dtype(dims)
+    D = d.d_c + d.d_rope
+    if workspace is not None and not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_cache_append", load().mla_cache_append(
+        ctypes.byref(d), int(d_model), _ptr(h, "h", st, d.batch * d.q_len * d_model),
+        _ptr(w_dkv, "w_dkv", st, d.d_c * d_model),
+        _ptr(w_kr, "w_kr", st, d.d_rope * d_model) if w_kr is not None else None, float(rope_base),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
+        _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D), ws_ptr, ws_bytes, _stream(stream)))

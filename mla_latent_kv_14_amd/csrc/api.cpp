@@ -18,6 +18,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxDModel = 1 << 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
@@ -292,6 +293,42 @@ int mla_combine_absorb_out(const mla_dims* d, int32_t num_splits, const float* o
   if (!force_generic() && mla::absorb_mfma_supported(*d))
     return to_status(mla::launch_absorb_out_mfma(*d, o_latent, w_uv, out, s));
   return to_status(mla::launch_absorb_out_generic(*d, o_latent, w_uv, out, s));
+}
+
+int mla_cache_append_workspace_bytes(const mla_dims* d, int32_t d_model, size_t* bytes) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr || d_model < 1 || d_model > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  size_t b = 0;
+  if (mla::append_mfma_supported(*d, d_model))  // float32 split-K partials [KS, B*Lq, d_c + d_rope]
+    b = (size_t)mla::append_max_ksplit() * d->batch * d->q_len * (d->d_c + d->d_rope) * sizeof(float);
+  *bytes = (b + 255) / 256 * 256;
+  return MLA_OK;
+}
+
+int mla_cache_append(const mla_dims* d, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                     float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d_model < 1 || d_model > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(h) || !ptr_ok(w_dkv) || (d->d_rope > 0 && !ptr_ok(w_kr)) || !ptr_ok(block_table) ||
+      !ptr_ok(seq_lens) || !ptr_ok(kv_cache))
+    return MLA_ERR_INVALID_ARG;
+  if (!(rope_base > 0.f) || rope_base == INFINITY) return MLA_ERR_INVALID_ARG;
+  size_t need = 0;
+  mla_cache_append_workspace_bytes(d, d_model, &need);
+  if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need)) return MLA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (!force_generic() && mla::append_mfma_supported(*d, d_model)) {
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != MLA_OK) return st;
+    return to_status(mla::launch_append_mfma(*d, d_model, cus, h, w_dkv, w_kr, rope_base, block_table, seq_lens,
+                                             kv_cache, static_cast<float*>(workspace), s));
+  }
+  return to_status(
+      mla::launch_append_generic(*d, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens, kv_cache, s));
 }
 
 int mla_combine_absorb_out_fused(const mla_dims* d, int32_t num_splits) {

@@ -42,4 +42,16 @@ int combine_out_max_splits();
 hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o_part, const float* lse_part,
                                    const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream);
 
+// cache append (append.hip): matrix-core split-K path for bf16 storage with
+// d_model % 128 == 0 and (d_c + d_rope) % 32 == 0, portable path otherwise
+bool append_mfma_supported(const mla_dims& d, int d_model);
+int append_max_ksplit();
+int append_ksplit(const mla_dims& d, int d_model, int cus, int* per_out);
+hipError_t launch_append_mfma(const mla_dims& d, int d_model, int cus, const void* h, const void* w_dkv,
+                              const void* w_kr, float rope_base, const int32_t* table, const int32_t* seq_lens,
+                              void* cache, float* part, hipStream_t stream);
+hipError_t launch_append_generic(const mla_dims& d, int d_model, const void* h, const void* w_dkv, const void* w_kr,
+                                 float rope_base, const int32_t* table, const int32_t* seq_lens, void* cache,
+                                 hipStream_t stream);
+
 }  // namespace mla

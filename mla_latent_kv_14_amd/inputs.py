@@ -22,6 +22,12 @@ Recipe:
     order is a random permutation; table rows are padded with -1;
   * cache slots past a sequence's length in its last block are poisoned
     (NaN by default) because nothing may read them.
+
+Cache-append inputs (``make_append_inputs``) come from a second generator,
+``PCG64([seed, 0xA99E])``, so adding them moves none of the draws above:
+hidden states h ~ N(0, 1) of width d_model (7168 for the DeepSeek-V3 shapes,
+the input width of the Guide's MLA topology figure), then W^DKV and W^KR ~
+N(0, 1)/sqrt(d_model) (fan-in d_model), rounded like the rest.
 """
 from __future__ import annotations
 
@@ -32,7 +38,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "Problem", "make_problem", "workload"]
+__all__ = ["Workload", "WORKLOADS", "Problem", "make_problem", "workload", "AppendInputs", "make_append_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -51,6 +57,7 @@ class Workload:
     block_size: int
     lengths: tuple  # ("fixed", (L0, L1, ...)) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
     seed_base: int
+    d_model: int = 7168  # hidden width h feeding the cache append
 
     @property
     def row_width(self) -> int:
@@ -65,7 +72,7 @@ class Workload:
 WORKLOADS = {
     w.name: w
     for w in [
-        Workload("tiny_f32", "f32", 2, 8, 64, 16, 32, 32, 1, 16, ("fixed", (37, 200)), 1000),
+        Workload("tiny_f32", "f32", 2, 8, 64, 16, 32, 32, 1, 16, ("fixed", (37, 200)), 1000, 96),
         Workload("single_4k_bf16", "bf16", 1, 128, 512, 64, 128, 128, 1, 64, ("fixed", (4096,)), 2000),
         Workload("batch64_1k8k_bf16", "bf16", 64, 128, 512, 64, 128, 128, 1, 64, ("uniform", 1024, 8192), 3000),
         Workload("long128k_bf16", "bf16", 4, 128, 512, 64, 128, 128, 1, 64, ("fixed", (131072,) * 4), 4000),
@@ -188,3 +195,32 @@ def make_problem(wl: Workload, seed: Optional[int] = None, *, poison: Optional[s
                 else:
                     raise ValueError(f"unknown poison {poison!r}")
     return Problem(wl, seed, lens, table, cache, q_nope, q_rope, w_uk, w_uv)
+
+
+ROPE_BASE = 10000.0  # the apply_rope base of the DeepSeek V4 Pro MLA module
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    """Inputs of one cache append.  Tensors live on the CPU in the storage dtype."""
+
+    d_model: int
+    h: torch.Tensor  # [B, Lq, d_model]
+    w_dkv: torch.Tensor  # [d_c, d_model]
+    w_kr: torch.Tensor  # [d_rope, d_model]
+    rope_base: float = ROPE_BASE
+
+    def f64(self, name: str) -> np.ndarray:
+        return getattr(self, name).to(torch.float64).numpy()
+
+
+def make_append_inputs(prob: Problem, d_model: Optional[int] = None) -> AppendInputs:
+    """Draw the hidden states and projection weights of the new tokens of ``prob``."""
+    wl = prob.wl
+    d_model = wl.d_model if d_model is None else int(d_model)
+    rng = np.random.Generator(np.random.PCG64([prob.seed, 0xA99E]))
+    h = _store(rng.standard_normal((wl.batch, wl.q_len, d_model)), wl.dtype)
+    inv = 1.0 / math.sqrt(d_model)
+    w_dkv = _store(rng.standard_normal((wl.d_c, d_model)) * inv, wl.dtype)
+    w_kr = _store(rng.standard_normal((wl.d_rope, d_model)) * inv, wl.dtype)
+    return AppendInputs(d_model, h, w_dkv, w_kr)

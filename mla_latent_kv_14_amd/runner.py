@@ -46,6 +46,21 @@ class DecodeRunner:
         self.lse = torch.empty((B, Lq, H), dtype=torch.float32, device=dev)
         self.u = torch.empty((B, Lq, H, wl.d_v), dtype=st, device=dev)
 
+    def setup_append(self, app):
+        """Upload the inputs of a cache append (``inputs.AppendInputs``) and size its workspace."""
+        dev = self.device
+        self.app = app
+        self.h = app.h.to(dev)
+        self.w_dkv = app.w_dkv.to(dev)
+        self.w_kr = app.w_kr.to(dev)
+        nbytes = libmla.mla_cache_append_workspace_bytes(self.dims, app.d_model)
+        self.append_ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=dev) if nbytes else None
+
+    def cache_append(self, stream=None):
+        """Write the new tokens' rows [W^DKV h | RoPE(W^KR h)] into self.cache."""
+        libmla.mla_cache_append(self.dims, self.app.d_model, self.h, self.w_dkv, self.w_kr, self.app.rope_base,
+                                self.block_table, self.seq_lens, self.cache, self.append_ws, stream)
+
     def absorb_q(self, stream=None):
         libmla.mla_absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uk, self.q_cat, stream)
 

@@ -153,3 +153,43 @@ def test_missing_library_fails_loudly(tmp_path):
             "try:\n    L.load()\nexcept RuntimeError as e:\n    print('raised')\n")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "raised" in r.stdout
+
+
+def test_cache_append_workspace_bytes():
+    bf = _dims(dtype=libmla.MLA_BF16, batch=64, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128,
+               block_size=64)
+    n = libmla.mla_cache_append_workspace_bytes(bf, 7168)
+    assert n % 256 == 0 and n >= 64 * 576 * 4  # float32 partials, at least one split
+    assert libmla.mla_cache_append_workspace_bytes(bf, 7168 + 8) == 0  # not a multiple of 128: portable kernel
+    assert libmla.mla_cache_append_workspace_bytes(_dims(), 96) == 0  # float32 storage: portable kernel
+    out = ctypes.c_size_t(0)
+    for dm in (0, -1, 1 << 17):
+        assert _call("mla_cache_append_workspace_bytes", ctypes.byref(bf), dm, ctypes.byref(out)) == -1
+    assert _call("mla_cache_append_workspace_bytes", ctypes.byref(bf), 7168, None) == -1
+
+
+def _append(d, **over):
+    args = dict(d_model=96, h=P(FAKE), w_dkv=P(FAKE), w_kr=P(FAKE), base=10000.0, table=P(FAKE), lens=P(FAKE),
+                cache=P(FAKE), ws=P(FAKE), ws_bytes=1 << 24)
+    args.update(over)
+    return _call("mla_cache_append", ctypes.byref(d), args["d_model"], args["h"], args["w_dkv"], args["w_kr"],
+                 ctypes.c_float(args["base"]), args["table"], args["lens"], args["cache"], args["ws"],
+                 args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over", [
+    {"h": None}, {"w_dkv": None}, {"w_kr": None}, {"table": None}, {"lens": None}, {"cache": None},
+    {"h": P(FAKE + 2)}, {"cache": P(FAKE + 8)}, {"d_model": 0}, {"d_model": 1 << 17},
+    {"base": 0.0}, {"base": -2.0}, {"base": float("nan")}, {"base": float("inf")},
+])
+def test_cache_append_invalid_args(over):
+    assert _append(_dims(), **over) == libmla.MLA_ERR_INVALID_ARG
+
+
+def test_cache_append_workspace_checked():
+    bf = _dims(dtype=libmla.MLA_BF16, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128, block_size=64)
+    need = libmla.mla_cache_append_workspace_bytes(bf, 256)
+    assert need > 0
+    assert _append(bf, d_model=256, ws=None) == -1
+    assert _append(bf, d_model=256, ws_bytes=need - 1) == -1
+    assert _append(bf, d_model=256, ws=P(FAKE + 4)) == -1
