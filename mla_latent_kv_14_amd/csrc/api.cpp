@@ -97,15 +97,16 @@ int decode_shape(const mla_dims& d, DecodeShape* out) {
       return MLA_OK;
     }
     case DecodeKind::Mfma: {
-      // one 144 KiB-LDS workgroup per CU; a range must amortise loading the
-      // queries (H*Lq rows of 1152 B) against the cache rows it streams.
-      // A piece of a sequence costs about as much as streaming
-      //   R * (1152 B of queries + 2048 B of partial result) * 2/3
-      // of cache (the rest overlaps), in 64-row tiles of 73728 B.
+      // one 144 KiB-LDS workgroup per CU; a range must amortise the fixed
+      // cost of a piece against the cache rows it streams.  Measured per
+      // phase on MI355X, a piece costs about 1.5 tiles of pipeline fill plus
+      // R * (1152 B of queries + 2048 B of partial result) at 0.9 times the
+      // cost of streaming as many bytes of cache, in 64-row tiles of 73728 B:
+      //   ov = round(1.5 + R * 3200 * 0.9 / 73728)   (7 at R = 128, 3 at R = 32)
       const int R = d.q_len * d.num_heads;
       out->grid = cus;
       out->min_chunk = (R > 32) ? 4 : 2;
-      const int ov = (int)(((int64_t)R * 3200 * 2 / 3 + 36864) / 73728);
+      const int ov = (int)(((int64_t)R * 2880 + 147456) / 73728);
       out->ov = ov < 1 ? 1 : ov;
       return MLA_OK;
     }

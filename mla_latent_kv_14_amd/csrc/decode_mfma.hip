@@ -116,15 +116,25 @@ __device__ __forceinline__ void mfma_a(f32x16& d, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void pad_mfma() {
   __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
-// value of lane l ^ 32 combined with this lane's value (v_permlane32_swap, no LDS)
-__device__ __forceinline__ float xmax32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+// Maximum of three scores with the hardware instruction.  fmaxf would first
+// quiet every operand that the compiler cannot prove canonical (one extra
+// VALU instruction per score taken straight from an MFMA accumulator); the
+// scores are never NaN (masked columns hold -inf), so the hardware maximum
+// gives the same value.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
-__device__ __forceinline__ float xsum32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// Two floats rounded to bf16 (nearest, ties to even), lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+// Keeps x computed where this stands: the MFMAs are volatile asm, so an empty
+// volatile asm that reads and writes x stays between the same two MFMAs.
+template <typename T> __device__ __forceinline__ void pin(T& x) { __asm__ volatile("" : "+v"(x)); }
 
 // The read-only inputs come as separate __restrict__ arguments so that the
 // compiler may read the schedule through the scalar cache.
@@ -333,10 +343,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         }
         // Sub-tile i+3 is copied during the score loop below, one 1 KiB piece
         // every fourth MFMA: a wave can queue only a few copies, and a burst of
-        // nine would stall it for their whole transfer.  Every copy is
-        // counted by the waits below (vmcnt), the sink's ones included.
-        // with no sub-tile i+3 the copies re-read the last sub-tile (in L2)
-        // into the sink, so every step of the loop issues the same code
+        // nine would stall it for their whole transfer.  When there is no
+        // sub-tile i+3 the copies re-read the last sub-tile (an L2 hit) into
+        // the sink, so every step issues the same code and every wait count
+        // below (vmcnt) is the same constant, the sink's copies included.
         const bool copy_on = i + 3 < n_sub;
         const uint8_t* copy_src = tile_src(copy_on ? i + 3 : n_sub - 1);
         const uint32_t copy_dst = copy_on ? (uint32_t)(uintptr_t)smem + ((i + 3) & (kStages - 1)) * kSubBytes + wave * 1024
@@ -352,31 +362,68 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
           }
         }
 
-        // ---- softmax(i) in pieces, interleaved with the scores of sub-tile i+1
-        float tm = 0.f, neg_m = 0.f, psum = 0.f;
+        // ---- softmax(i) in pieces, interleaved with the scores of sub-tile i+1.
+        // The wave issues in order, so a piece must not wait on a result it
+        // produced itself in front of the next MFMA: every instruction of a
+        // piece reads only values made at least one piece (one MFMA) earlier.
+        // The row maximum is a tree of independent max3s; score r is scaled
+        // and shifted in piece 13 + r, exponentiated in the next piece and
+        // summed and packed to bf16 in the one after.
+        float tm = 0.f, neg_m = 0.f, psum = 0.f, mn = 0.f, hr = 0.f;
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, a4 = 0.f, b0 = 0.f, b1 = 0.f;
+        uint32_t sw0 = 0u, sw1 = 0u;
+        float xs[16], pv[16];
+        uint32_t pw[8];  // P as bf16 pairs: word w holds scores 2w (low) and 2w + 1
         bf16x8 pb[2];
         auto piece = [&](int k) {
-          if (k == 0) tm = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
-          if (k >= 1 && k <= 3) {
-            tm = __builtin_fmaxf(tm, __builtin_fmaxf(sc[4 * k], sc[4 * k + 1]));
-            tm = __builtin_fmaxf(tm, __builtin_fmaxf(sc[4 * k + 2], sc[4 * k + 3]));
+          if (k == 0) a0 = max3f(sc[0], sc[1], sc[2]);
+          if (k == 1) a1 = max3f(sc[3], sc[4], sc[5]);
+          if (k == 2) a2 = max3f(sc[6], sc[7], sc[8]);
+          if (k == 3) a3 = max3f(sc[9], sc[10], sc[11]);
+          if (k == 4) a4 = max3f(sc[12], sc[13], sc[14]);
+          if (k == 5) b0 = max3f(a0, a1, a2);
+          if (k == 6) b1 = max3f(a3, a4, sc[15]);
+          if (k == 7) tm = max3f(b0, b1, b1);
+          if (k == 8 || k == 31) {  // exchange with the lane holding the other half of the row
+            const uint32_t x = __float_as_uint(k == 8 ? tm : psum);
+            auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+            sw0 = r[0];
+            sw1 = r[1];
           }
-          if (k == 4) {
-            tm = xmax32(tm) * qk_scale;  // scale > 0 keeps the order
-            m_seen = __builtin_fmaxf(m_seen, tm);
-            if (m == -INFINITY) m = tm;  // nothing accumulated yet for this row
-            overflow |= tm > m + kHeadroom;
-            neg_m = (m == -INFINITY) ? 0.f : -m;
+          if (k == 9) tm = max3f(__uint_as_float(sw0), __uint_as_float(sw1), __uint_as_float(sw1));
+          if (k == 10) tm *= qk_scale;  // scale > 0 keeps the order
+          if (k == 11) {
+            m_seen = max3f(m_seen, tm, tm);
+            mn = (m == -INFINITY) ? tm : m;  // nothing accumulated yet for this row
           }
-          if (k >= 5 && k < 21) {
-            const int r = k - 5;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], qk_scale, neg_m));
-            psum += p;
-            pb[r >> 3][r & 7] = (__bf16)p;
+          if (k == 12) {
+            hr = mn + kHeadroom;
+            neg_m = (mn == -INFINITY) ? 0.f : -mn;
+            m = mn;
           }
-          if (k == 21) l += xsum32(psum);
+          if (k == 13) overflow |= tm > hr;
+          if (k >= 13 && k < 31) {
+            const int j = k - 13;
+            if (j < 16) {
+              xs[j] = __builtin_fmaf(sc[j], qk_scale, neg_m);
+              pin(xs[j]);
+            }
+            if (j >= 1 && j <= 16) {
+              pv[j - 1] = __builtin_amdgcn_exp2f(xs[j - 1]);
+              pin(pv[j - 1]);
+            }
+            if (j >= 2) {
+              const int r = j - 2;
+              psum += pv[r];
+              if (r & 1) {
+                pw[r >> 1] = pack_bf16(pv[r - 1], pv[r]);
+                pin(pw[r >> 1]);
+              }
+            }
+          }
+          if (k == 32) l += __uint_as_float(sw0) + __uint_as_float(sw1);
         };
-        constexpr int kPieces = 22;
+        constexpr int kPieces = 33;
 
         f32x16 sn;
         if (nxt) {
@@ -399,6 +446,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
 #pragma unroll
           for (int k = 0; k < kPieces; ++k) piece(k);
         }
+        pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
         __asm__ volatile("s_nop 4" ::: "memory");  // VALU-written pb before its MFMA reads
 
         // ---- O^T += V^T . P^T for sub-tile i over this wave's columns
