@@ -202,6 +202,20 @@ def main():
     log(f"bench: {ms_step * 1e3:.1f} us/step ({'graph' if args.graph else 'eager'}); per call, eager (us): " +
         ", ".join(f"{n}={v:.1f}" for n, v in per_call_us.items()))
 
+    # the attention kernel's own duration: K launches back to back between two
+    # events on its stream, so that each launch's dispatch overlaps the previous
+    # kernel (the per-call events above also hold that latency); the roofline
+    # below divides by this
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for i in range(K):
+        r.decode_planned()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    decode_kernel_us = 1e3 * d0.elapsed_time(d1) / K
+    log(f"bench: attention kernel {decode_kernel_us:.1f} us per launch (back to back)")
+
     # the cache append (the step just before attention in a decode loop),
     # timed on its own: K back-to-back calls; it rewrites the same slots
     app = make_append_inputs(prob)
@@ -220,7 +234,7 @@ def main():
     log(f"bench: cache append {append_us:.1f} us/call (d_model={app.d_model})")
 
     alg_bytes, flops = algorithmic_work(prob)
-    dec_s = per_call_us["decode"] * 1e-6
+    dec_s = decode_kernel_us * 1e-6
     achieved_gbs = alg_bytes / dec_s / 1e9
     achieved_tflops = flops / dec_s / 1e12
     tokens = wl.batch * wl.q_len
@@ -248,7 +262,8 @@ def main():
                    "d_rope": wl.d_rope, "d_nope": wl.d_nope, "d_v": wl.d_v, "block_size": wl.block_size,
                    "context_tokens": prob.total_tokens, "lengths": " ".join(str(x) for x in wl.lengths),
                    "num_splits": r.num_splits},
-        "roofline": {"kernel": "mla_decode attention", "bound": "hbm", "achieved": achieved_gbs,
+        "roofline": {"kernel": "mla_decode attention", "kernel_us": decode_kernel_us, "bound": "hbm",
+                     "achieved": achieved_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
                      "mfma_tflops": achieved_tflops, "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
