@@ -86,6 +86,16 @@ def test_bf16_mtp2_h16_ragged():
     _full_check(make_problem(wl, 11))
 
 
+@pytest.mark.parametrize("heads,q_len", [(64, 1), (32, 2), (8, 2), (20, 1), (32, 1)])
+def test_bf16_row_groups(heads, q_len):
+    """64 query rows per sequence (two waves per 32-row group split the score
+    contraction) and 32 or fewer (four waves split it; 20 leaves rows past R
+    in the group): every element against the oracle."""
+    wl = workload("mtp2_lognormal_bf16", batch=6, heads=heads, q_len=q_len,
+                  lengths=("fixed", (2, 63, 65, 129, 700, 2049)))
+    _full_check(make_problem(wl, 13))
+
+
 def test_bf16_poison_big():
     wl = workload("single_4k_bf16", batch=2, lengths=("fixed", (70, 300)))
     _full_check(make_problem(wl, 12, poison="big"))
