@@ -50,6 +50,7 @@ __all__ = [
     "rope_reference",
     "cache_rows_reference",
     "cache_append_reference",
+    "prefill_reference",
 ]
 
 
@@ -291,3 +292,61 @@ def cache_append_reference(cache, block_table, seq_lens, h, w_dkv, w_kr, base=10
             out[int(block_table[b, t // bs]), t % bs, :] = row
     return out
 
+
+
+def prefill_reference(q_nope, q_rope, c_kv, k_rope, cu_seqlens, w_uk, w_uv, scale, causal=True, select=None):
+    """Non-absorbed MLA attention over whole sequences (prefill, training forward).
+
+    "Deconstructing DeepSeek V4 Pro ..." -- the forward pass of its MLA module
+    -- and "DeepSeek-V3 MLA: Multi-Head Latent Attention Guide" -- forward_train:
+    every token's latent is up-projected per head,
+        K_{t,h} = [W^UK_h c_t ; k^R_t],   V_{t,h} = W^UV_h c_t,
+    and u_{j,h} = softmax_t(scale q_{j,h} . K_{t,h}) V_{t,h} over the tokens of
+    j's own sequence, q_{j,h} = [q^C_{j,h} ; q^R_{j,h}].  Both pages' code
+    scores every key of the sequence; causal=True (the default) takes the
+    decoder's reading that token j sees the keys t <= j, as the decode step
+    does, and causal=False is the code as printed.
+
+    Tokens of all sequences are packed: sequence b is rows cu_seqlens[b] ..
+    cu_seqlens[b+1] - 1 of q_nope [T,H,d_n], q_rope [T,H,d_r], c_kv [T,d_c]
+    and k_rope [T,d_r] (already rotated).  w_uk [H,d_n,d_c], w_uv [H,d_v,d_c].
+    Returns (u [T,H,d_v], lse [T,H]) in float64, lse the natural-log
+    log-sum-exp of the scaled, masked scores.  ``select`` (iterable of
+    (token, head)) restricts the work to those pairs; the rest is NaN.
+    """
+    q_nope = np.asarray(q_nope, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    c_kv = np.asarray(c_kv, dtype=np.float64)
+    k_rope = np.asarray(k_rope, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, _ = q_nope.shape
+    d_v = w_uv.shape[1]
+    u = np.full((T, H, d_v), np.nan)
+    lse = np.full((T, H), np.nan)
+    wanted = None
+    if select is not None:
+        wanted = {}
+        for t, h in select:
+            wanted.setdefault(int(h), set()).add(int(t))
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 <= s0:
+            continue
+        c = c_kv[s0:s1]
+        for h in range(H):
+            rows = range(s0, s1) if wanted is None else sorted(t for t in wanted.get(h, ()) if s0 <= t < s1)
+            if not rows:
+                continue
+            keys = np.concatenate([c @ w_uk[h].T, k_rope[s0:s1]], axis=1)  # K_{t,h}, [L, d_n + d_r]
+            vals = c @ w_uv[h].T  # V_{t,h}, [L, d_v]
+            for t in rows:
+                j = t - s0  # position of the query inside its sequence
+                q = np.concatenate([q_nope[t, h], q_rope[t, h]])
+                n_vis = j + 1 if causal else s1 - s0  # keys 0 .. n_vis - 1
+                sc = scale * (keys[:n_vis] @ q)
+                p, lse_t = _softmax_stats(sc[None, :])
+                u[t, h] = p[0] @ vals[:n_vis]
+                lse[t, h] = lse_t[0]
+    return u, lse

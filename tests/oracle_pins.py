@@ -18,7 +18,11 @@ Independent routes used here:
   * for the cache append: RoPE as multiplication by a unit complex number
     (numpy complex arithmetic, angle from logarithms), RoPE's defining
     relative-position property, 2 x 2 rotation matrices in scalar loops, and
-    the paging invariant that only the new tokens' slots change.
+    the paging invariant that only the new tokens' slots change;
+  * for the prefill: the absorbed algebra per query token, torch's float64
+    scaled_dot_product_attention with is_causal, scalar loops, the decode
+    oracle on every prefix (a causal prefill row is a decode step), the key
+    permutation invariance of the unmasked form, and the one-key closed form.
 """
 from __future__ import annotations
 
@@ -353,6 +357,151 @@ def pin_cache_append(orc, seed=15):
                 _close(o[b, j, hh], (e / e.sum()) @ rows[:, : p.d_c])
 
 
+class TinyPrefill:
+    """Packed sequences for the prefill oracle (contiguous rows, no paging)."""
+
+    def __init__(self, seed=20, H=3, d_c=8, d_r=4, d_n=5, d_v=5, lens=(5, 1, 7)):
+        rng = np.random.default_rng(seed)
+        self.H, self.d_c, self.d_r, self.d_n, self.d_v = H, d_c, d_r, d_n, d_v
+        self.lens = np.asarray(lens, dtype=np.int64)
+        self.cu = np.concatenate([[0], np.cumsum(self.lens)]).astype(np.int64)
+        T = int(self.cu[-1])
+        self.c = rng.standard_normal((T, d_c))
+        self.kr = rng.standard_normal((T, d_r))
+        self.q_nope = rng.standard_normal((T, H, d_n))
+        self.q_rope = rng.standard_normal((T, H, d_r))
+        self.w_uk = rng.standard_normal((H, d_n, d_c)) / math.sqrt(d_c)
+        self.w_uv = rng.standard_normal((H, d_v, d_c)) / math.sqrt(d_c)
+        self.scale = 1.0 / math.sqrt(d_n + d_r)
+
+    def run(self, orc, causal=True, **kw):
+        return orc.prefill_reference(self.q_nope, self.q_rope, self.c, self.kr, self.cu, self.w_uk, self.w_uv,
+                                     self.scale, causal=causal, **kw)
+
+
+def pin_prefill_absorbed(orc, seed=20):
+    """Prefill u and lse equal the absorbed algebra token by token (q~ = W_UK^T q^C, scores on the
+    latents, W_UV applied after the latent-weighted sum), causal and unmasked."""
+    p = TinyPrefill(seed)
+    for causal in (True, False):
+        u, lse = p.run(orc, causal=causal)
+        for b in range(len(p.lens)):
+            s0, s1 = int(p.cu[b]), int(p.cu[b + 1])
+            for t in range(s0, s1):
+                vis = slice(s0, t + 1) if causal else slice(s0, s1)
+                for h in range(p.H):
+                    q_abs = np.einsum("n,nc->c", p.q_nope[t, h], p.w_uk[h])
+                    sc = (p.c[vis] @ q_abs + p.kr[vis] @ p.q_rope[t, h]) * p.scale
+                    w = np.exp(sc - sc.max())
+                    z = w.sum()
+                    _close(u[t, h], p.w_uv[h] @ ((w / z) @ p.c[vis]))
+                    _close(lse[t, h], sc.max() + math.log(z))
+
+
+def pin_prefill_sdpa(orc, seed=21):
+    """Prefill u equals torch's float64 scaled_dot_product_attention (is_causal for the causal form)."""
+    p = TinyPrefill(seed, H=4, lens=(9, 3, 6))
+    for causal in (True, False):
+        u, _ = p.run(orc, causal=causal)
+        for b in range(len(p.lens)):
+            s0, s1 = int(p.cu[b]), int(p.cu[b + 1])
+            L = s1 - s0
+            c = torch.from_numpy(p.c[s0:s1])
+            kr = torch.from_numpy(p.kr[s0:s1])
+            K = torch.cat([torch.einsum("tc,hnc->htn", c, torch.from_numpy(p.w_uk)),
+                           kr.unsqueeze(0).expand(p.H, L, p.d_r)], dim=2)
+            V = torch.einsum("tc,hvc->htv", c, torch.from_numpy(p.w_uv))
+            Q = torch.cat([torch.from_numpy(p.q_nope[s0:s1]), torch.from_numpy(p.q_rope[s0:s1])], dim=2).transpose(0, 1)
+            ref = torch.nn.functional.scaled_dot_product_attention(Q.contiguous(), K.contiguous(), V.contiguous(),
+                                                                   is_causal=causal, scale=p.scale)
+            _close(u[s0:s1], ref.transpose(0, 1).numpy())
+
+
+def pin_prefill_bruteforce(orc, seed=22):
+    """Prefill u equals scalar pure-Python loops on a tiny problem."""
+    p = TinyPrefill(seed, H=2, d_c=3, d_r=2, d_n=2, d_v=2, lens=(3, 2))
+    u, _ = p.run(orc)
+    for b in range(len(p.lens)):
+        s0, s1 = int(p.cu[b]), int(p.cu[b + 1])
+        for t in range(s0, s1):
+            for h in range(p.H):
+                scores = []
+                for k in range(s0, t + 1):
+                    acc = 0.0
+                    for n in range(p.d_n):
+                        kc = sum(p.w_uk[h, n, i] * p.c[k, i] for i in range(p.d_c))
+                        acc += p.q_nope[t, h, n] * kc
+                    for r in range(p.d_r):
+                        acc += p.q_rope[t, h, r] * p.kr[k, r]
+                    scores.append(acc * p.scale)
+                mx = max(scores)
+                ws = [math.exp(x - mx) for x in scores]
+                z = sum(ws)
+                for v in range(p.d_v):
+                    val = 0.0
+                    for k, w in zip(range(s0, t + 1), ws):
+                        val += w / z * sum(p.w_uv[h, v, i] * p.c[k, i] for i in range(p.d_c))
+                    assert abs(u[t, h, v] - val) <= 1e-11 * max(1.0, abs(val)), (t, h, v)
+
+
+def pin_prefill_matches_decode(orc, seed=23):
+    """A causal prefill row is a decode step: row t equals the decode oracle over the prefix
+    0..t of its sequence, with that token as the single new query (blocks in order)."""
+    p = TinyPrefill(seed, lens=(6, 4))
+    u, lse = p.run(orc)
+    bs = 2
+    for b in range(len(p.lens)):
+        s0, s1 = int(p.cu[b]), int(p.cu[b + 1])
+        for t in range(s0, s1):
+            n = t - s0 + 1
+            rows = np.concatenate([p.c[s0:t + 1], p.kr[s0:t + 1]], axis=1)
+            nb = (n + bs - 1) // bs
+            cache = np.full((nb, bs, rows.shape[1]), np.nan)
+            for i in range(n):
+                cache[i // bs, i % bs] = rows[i]
+            table = np.arange(nb).reshape(1, nb)
+            ud, _, ld = orc.mla_decode_reference(p.q_nope[t][None, None], p.q_rope[t][None, None], cache, table,
+                                                 np.array([n]), p.w_uk, p.w_uv, p.scale, p.d_c)
+            _close(u[t], ud[0, 0])
+            _close(lse[t], ld[0, 0])
+
+
+def pin_prefill_key_permutation(orc, seed=24):
+    """Without the mask, permuting a sequence's keys and values together (its c and k^R rows)
+    changes nothing; with the mask, the first token's output depends on the first key only."""
+    p = TinyPrefill(seed)
+    u, lse = p.run(orc, causal=False)
+    rng = np.random.default_rng(seed)
+    q = TinyPrefill(seed)
+    for b in range(len(p.lens)):
+        s0, s1 = int(p.cu[b]), int(p.cu[b + 1])
+        perm = s0 + rng.permutation(s1 - s0)
+        q.c[s0:s1] = p.c[perm]
+        q.kr[s0:s1] = p.kr[perm]
+    u2, lse2 = q.run(orc, causal=False)
+    _close(u2, u, rtol=1e-10, atol=1e-11)
+    _close(lse2, lse, rtol=1e-10, atol=1e-11)
+    uc, lc = p.run(orc, causal=True)
+    for b in range(len(p.lens)):
+        t = int(p.cu[b])
+        for h in range(p.H):
+            _close(uc[t, h], p.w_uv[h] @ p.c[t])  # one visible key: weight 1
+            k = np.concatenate([p.w_uk[h] @ p.c[t], p.kr[t]])
+            _close(lc[t, h], p.scale * float(np.concatenate([p.q_nope[t, h], p.q_rope[t, h]]) @ k))
+
+
+def pin_prefill_select(orc, seed=25):
+    """Restricting the prefill to chosen (token, head) pairs reproduces those entries."""
+    p = TinyPrefill(seed)
+    u, lse = p.run(orc)
+    sel = [(0, 1), (5, 0), (11, 2), (7, 1)]
+    us, ls = p.run(orc, select=sel)
+    for t, h in sel:
+        _close(us[t, h], u[t, h])
+        _close(ls[t, h], lse[t, h])
+    assert np.isnan(us[1, 0]).all()
+
+
 ALL_PINS = [
     pin_absorbed_route,
     pin_library_sdpa,
@@ -370,4 +519,10 @@ ALL_PINS = [
     pin_rope_relative,
     pin_cache_rows_bruteforce,
     pin_cache_append,
+    pin_prefill_absorbed,
+    pin_prefill_sdpa,
+    pin_prefill_bruteforce,
+    pin_prefill_matches_decode,
+    pin_prefill_key_permutation,
+    pin_prefill_select,
 ]

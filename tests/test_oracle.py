@@ -98,6 +98,14 @@ MUTATIONS = {
                             "k = h @ np.asarray(w_kr, dtype=np.float64).T"),
     "append_wdkv_transposed": ("c = h @ np.asarray(w_dkv, dtype=np.float64).T",
                                "c = (np.asarray(w_dkv, dtype=np.float64) @ np.resize(h, np.asarray(w_dkv).shape[1]))[..., : np.asarray(w_dkv).shape[0]] * 0 + h[..., : np.asarray(w_dkv).shape[0]]"),
+    "prefill_causal_off_by_one": ("n_vis = j + 1 if causal else s1 - s0", "n_vis = j + 2 if causal else s1 - s0"),
+    "prefill_rope_dropped": ("keys = np.concatenate([c @ w_uk[h].T, k_rope[s0:s1]], axis=1)",
+                             "keys = np.concatenate([c @ w_uk[h].T, 0.0 * k_rope[s0:s1]], axis=1)"),
+    "prefill_values_from_w_uk": ("vals = c @ w_uv[h].T", "vals = c @ w_uk[h].T"),
+    "prefill_global_position": ("j = t - s0  #", "j = t  #"),
+    "prefill_missing_scale": ("sc = scale * (keys[:n_vis] @ q)", "sc = keys[:n_vis] @ q"),
+    "prefill_rope_query_dropped": ("q = np.concatenate([q_nope[t, h], q_rope[t, h]])\n                n_vis",
+                                   "q = np.concatenate([q_nope[t, h], 0.0 * q_rope[t, h]])\n                n_vis"),
 }
 
 
