@@ -218,6 +218,44 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
                      float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- prefill: the non-absorbed forward over whole sequences ------------ */
+
+/* Bytes of device workspace mla_prefill needs for these dims and
+ * total_tokens: the per-head up-projected keys and values and a copy of the
+ * RoPE keys, T * (H * (d_nope + d_v) + d_rope) elements of the storage type.
+ * Host only. */
+int mla_prefill_workspace_bytes(const mla_dims* dims, int32_t total_tokens, size_t* bytes);
+
+/* Attention of every token of every sequence over its own sequence, in the
+ * non-absorbed form ("Deconstructing DeepSeek V4 Pro", the forward pass of
+ * its MLA module; "DeepSeek-V3 MLA: Multi-Head Latent Attention Guide",
+ * forward_train):
+ *   K_{t,h} = [W^UK_h c_t ; k^R_t],  V_{t,h} = W^UV_h c_t,
+ *   u_{j,h} = softmax_t(scale * [q^C_{j,h}; q^R_{j,h}] . K_{t,h}) V_{t,h}
+ * over the tokens t of j's sequence, t <= j when causal = 1 (a decoder's
+ * prefill), all of them when causal = 0 (the pages' code as printed).
+ * Tokens of the dims->batch sequences are packed: sequence b is tokens
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1.
+ *   cu_seqlens [B+1] int32 (device), non-decreasing, cu_seqlens[0] = 0,
+ *              cu_seqlens[B] = total_tokens; no sequence longer than max_seqlen
+ *   q_nope [T,H,d_nope], q_rope [T,H,d_rope]  queries, storage type
+ *   c_kv   [T,d_c], k_rope [T,d_rope]         the tokens' cache rows
+ *                                             (latent and rotated RoPE key)
+ *   w_uk [H,d_nope,d_c], w_uv [H,d_v,d_c]     storage type
+ *   out    [T,H,d_v] storage type;  lse [T,H] float32 (natural log), or NULL
+ *   workspace  at least mla_prefill_workspace_bytes(); overwritten
+ * Only dims->batch, num_heads, d_c, d_rope, d_nope, d_v and dtype are used
+ * (the other fields must still be valid, e.g. 1).  Products accumulate in
+ * float32; the up-projected K and V are rounded once to the storage type, and
+ * for bf16 the softmax weights are rounded to bf16 before the weighted sum.
+ * A sequence longer than max_seqlen or a cu_seqlens outside [0, T] is
+ * undefined behaviour (reads stay inside the buffers).  MLA_ERR_UNSUPPORTED
+ * when the bf16 workspace would reach 4 GiB (split the batch). */
+int mla_prefill(const mla_dims* dims, int32_t total_tokens, int32_t max_seqlen, const int32_t* cu_seqlens,
+                const void* q_nope, const void* q_rope, const void* c_kv, const void* k_rope, const void* w_uk,
+                const void* w_uv, float softmax_scale, int32_t causal, void* out, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* mla_status_str(int status);
 

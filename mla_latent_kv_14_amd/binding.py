@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         "mla_combine_absorb_out_fused": [D, I32],
         "mla_cache_append_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_cache_append": [D, I32, P, P, P, F32, P, P, P, P, SZ, P],
+        "mla_prefill_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
+        "mla_prefill": [D, I32, I32, P, P, P, P, P, P, P, F32, I32, P, P, P, SZ, P],
         "mla_version": [],
     }
     for name, args in sig.items():
@@ -247,3 +249,26 @@ def mla_cache_append(dims, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def mla_prefill_workspace_bytes(dims, total_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_prefill_workspace_bytes",
+           load().mla_prefill_workspace_bytes(ctypes.byref(dims), int(total_tokens), ctypes.byref(out)))
+    return out.value
+
+
+def mla_prefill(dims, total_tokens, max_seqlen, cu_seqlens, q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, softmax_scale,
+                causal, out, workspace, lse=None, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    T, H = int(total_tokens), d.num_heads
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_prefill", load().mla_prefill(
+        ctypes.byref(d), T, int(max_seqlen), _ptr(cu_seqlens, "cu_seqlens", torch.int32, d.batch + 1),
+        _ptr(q_nope, "q_nope", st, T * H * d.d_nope), _ptr(q_rope, "q_rope", st, T * H * d.d_rope),
+        _ptr(c_kv, "c_kv", st, T * d.d_c), _ptr(k_rope, "k_rope", st, T * d.d_rope),
+        _ptr(w_uk, "w_uk", st, H * d.d_nope * d.d_c), _ptr(w_uv, "w_uv", st, H * d.d_v * d.d_c),
+        float(softmax_scale), int(causal), _ptr(out, "out", st, T * H * d.d_v),
+        _ptr(lse, "lse", torch.float32, T * H) if lse is not None else None,
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -332,6 +332,36 @@ int mla_cache_append(const mla_dims* d, int32_t d_model, const void* h, const vo
       mla::launch_append_generic(*d, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens, kv_cache, s));
 }
 
+int mla_prefill_workspace_bytes(const mla_dims* d, int32_t total_tokens, size_t* bytes) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr || total_tokens < 1) return MLA_ERR_INVALID_ARG;
+  *bytes = (size_t)mla::prefill_layout(*d, total_tokens).total_bytes;
+  return MLA_OK;
+}
+
+int mla_prefill(const mla_dims* d, int32_t total_tokens, int32_t max_seqlen, const int32_t* cu_seqlens,
+                const void* q_nope, const void* q_rope, const void* c_kv, const void* k_rope, const void* w_uk,
+                const void* w_uv, float softmax_scale, int32_t causal, void* out, float* lse, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (total_tokens < 1 || max_seqlen < 1 || max_seqlen > total_tokens || (causal != 0 && causal != 1))
+    return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(cu_seqlens) || !ptr_ok(q_nope) || !ptr_ok(c_kv) || !ptr_ok(w_uk) || !ptr_ok(w_uv) || !ptr_ok(out) ||
+      !ptr_ok(workspace) || (d->d_rope > 0 && (!ptr_ok(q_rope) || !ptr_ok(k_rope))) ||
+      (lse != nullptr && !aligned16(lse)))
+    return MLA_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MLA_ERR_INVALID_ARG;
+  const mla::PrefillLayout lay = mla::prefill_layout(*d, total_tokens);
+  if (workspace_bytes < (size_t)lay.total_bytes) return MLA_ERR_INVALID_ARG;
+  const bool mfma = !force_generic() && mla::prefill_mfma_supported(*d);
+  // the matrix-core kernels address the workspace with 32-bit byte offsets
+  if (mfma && lay.total_bytes >= ((int64_t)1 << 32)) return MLA_ERR_UNSUPPORTED;
+  return to_status(mla::launch_prefill(*d, total_tokens, max_seqlen, cu_seqlens, q_nope, q_rope, c_kv, k_rope, w_uk,
+                                       w_uv, softmax_scale, causal, out, lse, workspace, mfma, (hipStream_t)stream));
+}
+
 int mla_combine_absorb_out_fused(const mla_dims* d, int32_t num_splits) {
   if (check_dims(d) != MLA_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
   return (!force_generic() && mla::absorb_mfma_supported(*d) && num_splits <= mla::combine_out_max_splits()) ? 1 : 0;

@@ -38,15 +38,10 @@
 // reads (4 rows x 4 chunks) over all 64 banks.
 #include "common.h"
 #include "internal.h"
+#include "mfma_util.h"
 
 namespace mla {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kDC = 512;
 constexpr int kDR = 64;
@@ -67,29 +62,15 @@ constexpr float kHeadroom = 64.0f;  // log2 units a score may exceed the referen
 // many steps ahead of their MFMA; deeper rings measured slower)
 constexpr int kOperandAhead = 4;
 
-__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
-
 // byte offset of (row, logical 16-B chunk) inside a sub-tile buffer
 __device__ __forceinline__ int tile_off(int r, int c) { return (r * kChunks + (c ^ swz(r))) * 16; }
 
-// s_waitcnt vmcnt(N) with expcnt/lgkmcnt left at their maxima (no wait on them)
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void vm_wait(int n) {
+__device__ __forceinline__ void vm_wait_n(int n) {  // n in {0, 9, 18}
   switch (n) {
     case 0: vm_wait<0>(); break;
     case 9: vm_wait<9>(); break;
     default: vm_wait<18>(); break;
   }
-}
-
-__device__ __forceinline__ void block_sync() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
 }
 
 // ===================================================================================
@@ -102,39 +83,6 @@ __device__ __forceinline__ void block_sync() {
 // flight.  The compiler does not see these as MFMAs, so the wait states a
 // VALU read of an MFMA result needs are inserted explicitly (pad_mfma) where
 // such a read can follow closely.
-
-__device__ __forceinline__ void mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_a(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-// 64 wait states: more than any MFMA result latency on this part
-__device__ __forceinline__ void pad_mfma() {
-  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-// Maximum of three scores with the hardware instruction.  fmaxf would first
-// quiet every operand that the compiler cannot prove canonical (one extra
-// VALU instruction per score taken straight from an MFMA accumulator); the
-// scores are never NaN (masked columns hold -inf), so the hardware maximum
-// gives the same value.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-// Two floats rounded to bf16 (nearest, ties to even), lo in the low half.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-// Keeps x computed where this stands: the MFMAs are volatile asm, so an empty
-// volatile asm that reads and writes x stays between the same two MFMAs.
-template <typename T> __device__ __forceinline__ void pin(T& x) { __asm__ volatile("" : "+v"(x)); }
 
 // The read-only inputs come as separate __restrict__ arguments so that the
 // compiler may read the schedule through the scalar cache.
@@ -311,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       };
 
       // ---- prologue: sub-tile 0 ready, its scores computed
-      vm_wait(min(2, n_sub - 1) * 9);
+      vm_wait_n(min(2, n_sub - 1) * 9);
       block_sync();
       fix_partial(0);
       f32x16 sc;
@@ -337,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         const int t0 = seg.tok_begin + i * kSub;
         const bool nxt = i + 1 < n_sub;
         if (nxt) {
-          vm_wait(i + 2 < n_sub ? 9 : 0);
+          vm_wait_n(i + 2 < n_sub ? 9 : 0);
           block_sync();  // sub-tile i+1 landed; every wave is past PV(i-1)
           fix_partial(i + 1);
         }

@@ -54,4 +54,17 @@ hipError_t launch_append_generic(const mla_dims& d, int d_model, const void* h, 
                                  float rope_base, const int32_t* table, const int32_t* seq_lens, void* cache,
                                  hipStream_t stream);
 
+// prefill (prefill.hip): matrix-core path for bf16 with d_c = 512, d_rope = 64,
+// d_nope = d_v = 128; portable path otherwise
+struct PrefillLayout {
+  int64_t v_off, r_off;  // element offsets of V and R in the workspace (Kn at 0)
+  int64_t total_bytes;
+};
+bool prefill_mfma_supported(const mla_dims& d);
+PrefillLayout prefill_layout(const mla_dims& d, int64_t tokens);
+hipError_t launch_prefill(const mla_dims& d, int tokens, int max_seqlen, const int32_t* cu, const void* q_nope,
+                          const void* q_rope, const void* c_kv, const void* k_rope, const void* w_uk,
+                          const void* w_uv, float scale, int causal, void* out, float* lse, void* ws, bool mfma,
+                          hipStream_t stream);
+
 }  // namespace mla

@@ -28,6 +28,12 @@ Cache-append inputs (``make_append_inputs``) come from a second generator,
 hidden states h ~ N(0, 1) of width d_model (7168 for the DeepSeek-V3 shapes,
 the input width of the Guide's MLA topology figure), then W^DKV and W^KR ~
 N(0, 1)/sqrt(d_model) (fan-in d_model), rounded like the rest.
+
+Prefill problems (``make_prefill_problem``, the prefill_* workloads) come
+from ``PCG64([seed, 0x9F11])``: lengths by the workload's distribution, then
+the tokens' latents c ~ N(0, 1), RoPE keys ~ N(0, 1), q_nope, q_rope ~ N(0, 1)
+per (token, head), then W_UK, W_UV ~ N(0, 1)/sqrt(d_c); the tokens of all
+sequences are packed in sequence order.
 """
 from __future__ import annotations
 
@@ -38,7 +44,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "Problem", "make_problem", "workload", "AppendInputs", "make_append_inputs"]
+__all__ = ["Workload", "WORKLOADS", "Problem", "make_problem", "workload", "AppendInputs", "make_append_inputs",
+           "PrefillProblem", "make_prefill_problem"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -78,6 +85,10 @@ WORKLOADS = {
         Workload("long128k_bf16", "bf16", 4, 128, 512, 64, 128, 128, 1, 64, ("fixed", (131072,) * 4), 4000),
         Workload("mtp2_lognormal_bf16", "bf16", 128, 16, 512, 64, 128, 128, 2, 64,
                  ("lognormal", 2048, 1.0, 64, 32768), 5000),
+        # prefill (whole sequences as queries; q_len and block_size unused)
+        Workload("prefill_tiny_f32", "f32", 3, 4, 64, 16, 32, 32, 1, 16, ("fixed", (5, 1, 70)), 6000, 96),
+        Workload("prefill_4x4k_bf16", "bf16", 4, 128, 512, 64, 128, 128, 1, 64, ("fixed", (4096,) * 4), 7000),
+        Workload("prefill_mixed_bf16", "bf16", 8, 128, 512, 64, 128, 128, 1, 64, ("uniform", 128, 4096), 8000),
     ]
 }
 
@@ -224,3 +235,51 @@ def make_append_inputs(prob: Problem, d_model: Optional[int] = None) -> AppendIn
     w_dkv = _store(rng.standard_normal((wl.d_c, d_model)) * inv, wl.dtype)
     w_kr = _store(rng.standard_normal((wl.d_rope, d_model)) * inv, wl.dtype)
     return AppendInputs(d_model, h, w_dkv, w_kr)
+
+
+@dataclasses.dataclass
+class PrefillProblem:
+    """One drawn prefill problem: whole sequences, tokens packed.  CPU tensors, storage dtype."""
+
+    wl: Workload
+    seed: int
+    seq_lens: np.ndarray  # int32 [B]
+    cu_seqlens: np.ndarray  # int32 [B + 1]
+    q_nope: torch.Tensor  # [T, H, d_nope]
+    q_rope: torch.Tensor  # [T, H, d_rope]
+    c_kv: torch.Tensor  # [T, d_c]
+    k_rope: torch.Tensor  # [T, d_rope]
+    w_uk: torch.Tensor  # [H, d_nope, d_c]
+    w_uv: torch.Tensor  # [H, d_v, d_c]
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def scale(self) -> float:
+        return self.wl.scale
+
+    def f64(self, name: str) -> np.ndarray:
+        return getattr(self, name).to(torch.float64).numpy()
+
+
+def make_prefill_problem(wl: Workload, seed: Optional[int] = None, seq_lens: Optional[np.ndarray] = None) -> PrefillProblem:
+    """Draw one prefill problem; ``seq_lens`` overrides the drawn lengths (drawn first all the same)."""
+    seed = wl.seed_base if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64([seed, 0x9F11]))
+    lens = _draw_lengths(wl, rng)
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int32)
+        if lens.shape != (wl.batch,) or (lens < 0).any():
+            raise ValueError("bad seq_lens override")
+    cu = np.concatenate([[0], np.cumsum(lens.astype(np.int64))]).astype(np.int32)
+    T = int(cu[-1])
+    c_kv = _store(rng.standard_normal((T, wl.d_c)), wl.dtype)
+    k_rope = _store(rng.standard_normal((T, wl.d_rope)), wl.dtype)
+    q_nope = _store(rng.standard_normal((T, wl.heads, wl.d_nope)), wl.dtype)
+    q_rope = _store(rng.standard_normal((T, wl.heads, wl.d_rope)), wl.dtype)
+    inv = 1.0 / math.sqrt(wl.d_c)
+    w_uk = _store(rng.standard_normal((wl.heads, wl.d_nope, wl.d_c)) * inv, wl.dtype)
+    w_uv = _store(rng.standard_normal((wl.heads, wl.d_v, wl.d_c)) * inv, wl.dtype)
+    return PrefillProblem(wl, seed, lens, cu, q_nope, q_rope, c_kv, k_rope, w_uk, w_uv)

@@ -119,3 +119,31 @@ class DecodeRunner:
         self.decode(stream)
         self.combine(stream)
         self.absorb_out(stream)
+
+
+class PrefillRunner:
+    """Device-resident buffers for one prefill problem and the mla_prefill call."""
+
+    def __init__(self, prob, device="cuda", causal=True):
+        self.prob = prob
+        wl = prob.wl
+        self.device = torch.device(device)
+        self.causal = bool(causal)
+        st = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        self.dims = libmla.make_dims(wl.batch, 1, wl.heads, wl.d_c, wl.d_rope, wl.d_nope, wl.d_v, 1, 1, 1, st)
+        dev = self.device
+        T = prob.total_tokens
+        self.cu = torch.from_numpy(np.ascontiguousarray(prob.cu_seqlens)).to(dev)
+        self.q_nope, self.q_rope = prob.q_nope.to(dev), prob.q_rope.to(dev)
+        self.c_kv, self.k_rope = prob.c_kv.to(dev), prob.k_rope.to(dev)
+        self.w_uk, self.w_uv = prob.w_uk.to(dev), prob.w_uv.to(dev)
+        self.max_seqlen = max(int(prob.seq_lens.max()), 1)
+        nbytes = libmla.mla_prefill_workspace_bytes(self.dims, T)
+        self.workspace = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+        self.u = torch.empty((T, wl.heads, wl.d_v), dtype=st, device=dev)
+        self.lse = torch.empty((T, wl.heads), dtype=torch.float32, device=dev)
+
+    def prefill(self, stream=None):
+        libmla.mla_prefill(self.dims, self.prob.total_tokens, self.max_seqlen, self.cu, self.q_nope, self.q_rope,
+                           self.c_kv, self.k_rope, self.w_uk, self.w_uv, self.prob.scale, self.causal, self.u,
+                           self.workspace, self.lse, stream)

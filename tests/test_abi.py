@@ -193,3 +193,40 @@ def test_cache_append_workspace_checked():
     assert _append(bf, d_model=256, ws=None) == -1
     assert _append(bf, d_model=256, ws_bytes=need - 1) == -1
     assert _append(bf, d_model=256, ws=P(FAKE + 4)) == -1
+
+
+def test_prefill_workspace_bytes():
+    bf = _dims(dtype=libmla.MLA_BF16, batch=4, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128)
+    n = libmla.mla_prefill_workspace_bytes(bf, 16384)
+    assert n >= 16384 * (128 * 256 + 64) * 2 and n % 256 == 0
+    out = ctypes.c_size_t(0)
+    assert _call("mla_prefill_workspace_bytes", ctypes.byref(bf), 0, ctypes.byref(out)) == -1
+    assert _call("mla_prefill_workspace_bytes", ctypes.byref(bf), 16, None) == -1
+
+
+def _prefill(d, **over):
+    args = dict(T=100, maxlen=60, cu=P(FAKE), qn=P(FAKE), qr=P(FAKE), c=P(FAKE), kr=P(FAKE), wk=P(FAKE),
+                wv=P(FAKE), scale=0.1, causal=1, out=P(FAKE), lse=None, ws=P(FAKE), ws_bytes=1 << 30)
+    args.update(over)
+    return _call("mla_prefill", ctypes.byref(d), args["T"], args["maxlen"], args["cu"], args["qn"], args["qr"],
+                 args["c"], args["kr"], args["wk"], args["wv"], ctypes.c_float(args["scale"]), args["causal"],
+                 args["out"], args["lse"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over", [
+    {"cu": None}, {"qn": None}, {"qr": None}, {"c": None}, {"kr": None}, {"wk": None}, {"wv": None},
+    {"out": None}, {"ws": None}, {"qn": P(FAKE + 2)}, {"lse": P(FAKE + 4)},
+    {"T": 0}, {"maxlen": 0}, {"maxlen": 101}, {"causal": 2}, {"causal": -1},
+    {"scale": 0.0}, {"scale": float("nan")}, {"scale": float("inf")}, {"ws_bytes": 1024},
+])
+def test_prefill_invalid_args(over):
+    assert _prefill(_dims(), **over) == libmla.MLA_ERR_INVALID_ARG
+
+
+def test_prefill_bf16_workspace_limit():
+    # the matrix-core kernels address the workspace with 32-bit offsets
+    bf = _dims(dtype=libmla.MLA_BF16, batch=1, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128)
+    T = 70000
+    need = libmla.mla_prefill_workspace_bytes(bf, T)
+    assert need >= 1 << 32
+    assert _prefill(bf, T=T, maxlen=T, ws_bytes=need) == libmla.MLA_ERR_UNSUPPORTED
