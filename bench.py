@@ -3,10 +3,13 @@
 
 A step is one pass of the whole hot path over one batch: plan, absorb_q,
 split-KV attention, then the log-sum-exp combine and absorb_out (one fused
-call), for every sequence of the workload.  Inputs are seeded synthetic tensors already resident in HBM.
+call), for every sequence of the workload.  Inputs are seeded synthetic
+tensors already resident in HBM.  The same line also reports, measured on
+their own: the cache append of the step's new tokens and the prefill of a
+4 x 4096-token batch (--no-prefill skips it).
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-prefill]
 """
 from __future__ import annotations
 
@@ -26,7 +29,9 @@ sys.path.insert(0, ROOT)
 DEFAULT_WORKLOAD = "batch64_1k8k_bf16"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-KERNEL_SOURCES = ["mla_latent_kv_14_amd/csrc/decode_mfma.hip", "mla_latent_kv_14_amd/csrc/common.h"]
+KERNEL_SOURCES = ["mla_latent_kv_14_amd/csrc/decode_mfma.hip", "mla_latent_kv_14_amd/csrc/common.h",
+                  "mla_latent_kv_14_amd/csrc/mfma_util.h"]
+PREFILL_WORKLOAD = "prefill_4x4k_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_batch64_1k8k_traffic.json")
 
 
@@ -66,6 +71,17 @@ def append_work(prob, d_model):
     M = wl.batch * wl.q_len
     nbytes = (D * d_model + M * d_model + M * D) * esz + M * 4 + wl.batch * 4
     return nbytes, 2 * M * D * d_model
+
+
+def prefill_work(prob):
+    """Flops of one prefill call: the attention over the visible (query, key)
+    pairs, (d_nope + d_rope + d_v) multiply-adds each per head, and the
+    up-projection of every token's latent to per-head keys and values."""
+    wl = prob.wl
+    causal_pairs = sum(int(L) * (int(L) + 1) // 2 for L in prob.seq_lens)
+    attn = 2 * wl.heads * causal_pairs * (wl.d_nope + wl.d_rope + wl.d_v)
+    up = 2 * prob.total_tokens * wl.d_c * wl.heads * (wl.d_nope + wl.d_v)
+    return attn, up
 
 
 def source_hash():
@@ -133,6 +149,7 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays instead of eager launches")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -142,8 +159,8 @@ def main():
 
     import torch
 
-    from mla_latent_kv_14_amd.inputs import make_append_inputs, make_problem, workload
-    from mla_latent_kv_14_amd.runner import DecodeRunner
+    from mla_latent_kv_14_amd.inputs import make_append_inputs, make_prefill_problem, make_problem, workload
+    from mla_latent_kv_14_amd.runner import DecodeRunner, PrefillRunner
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
@@ -233,6 +250,31 @@ def main():
     ap_bytes, ap_flops = append_work(prob, app.d_model)
     log(f"bench: cache append {append_us:.1f} us/call (d_model={app.d_model})")
 
+    # prefill (the non-absorbed forward over whole sequences), its own workload
+    prefill = None
+    if not args.no_prefill:
+        pprob = make_prefill_problem(workload(PREFILL_WORKLOAD))
+        pr = PrefillRunner(pprob, device="cuda:0")
+        for _ in range(2):
+            pr.prefill()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        KP = 5
+        torch.cuda.synchronize()
+        p0.record(stream)
+        for i in range(KP):
+            pr.prefill()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        pms = p0.elapsed_time(p1) / KP
+        f_attn, f_up = prefill_work(pprob)
+        prefill = {"workload": PREFILL_WORKLOAD, "tokens": pprob.total_tokens, "heads": pprob.wl.heads,
+                   "causal": True, "ms_per_call": pms, "tokens_per_s": pprob.total_tokens / (pms * 1e-3),
+                   "attn_tflop": f_attn / 1e12, "upproject_tflop": f_up / 1e12,
+                   "tflops": (f_attn + f_up) / (pms * 1e-3) / 1e12,
+                   "mfma_frac": (f_attn + f_up) / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        log(f"bench: prefill {PREFILL_WORKLOAD}: {pms:.2f} ms, {prefill['tflops']:.0f} TFLOP/s")
+        del pr
+
     alg_bytes, flops = algorithmic_work(prob)
     dec_s = decode_kernel_us * 1e-6
     achieved_gbs = alg_bytes / dec_s / 1e9
@@ -272,6 +314,7 @@ def main():
         "step_tflops": flops / (ms_step * 1e-3) / 1e12,
         "step_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "cache_append": {"us_per_call": append_us, "d_model": app.d_model, "alg_bytes": ap_bytes,
                          "gbs": ap_bytes / (append_us * 1e-6) / 1e9,
                          "hbm_frac": ap_bytes / (append_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
