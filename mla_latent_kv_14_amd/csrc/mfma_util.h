@@ -39,15 +39,20 @@ __device__ __forceinline__ void block_sync() {
 // 32x32x16 bf16 MFMAs written as inline asm so that the accumulator's
 // register class is fixed: v0 starts a VGPR accumulator at zero, v adds into
 // one, a adds into an AGPR accumulator.  The compiler does not see these as
-// MFMAs, so a VALU or LDS read of their result must be padded (pad_mfma).
+// MFMAs, so it inserts none of the wait states an MFMA needs around it:
+//  - before: an MFMA may read a VGPR only two wait states after a VALU
+//    instruction wrote it, and the compiler is free to produce an operand
+//    with a VALU copy right before the asm (an AGPR read-back when registers
+//    run short), so every wrapper opens with s_nop 1;
+//  - after: a VALU or LDS access of the result must be padded (pad_mfma).
 __device__ __forceinline__ void mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  __asm__ volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  __asm__ volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma_a(f32x16& d, const bf16x8& a, const bf16x8& b) {
-  __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+  __asm__ volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 // 64 wait states: more than any MFMA result latency on this part
 __device__ __forceinline__ void pad_mfma() {

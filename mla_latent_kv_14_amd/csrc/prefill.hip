@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -244,23 +245,34 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_mfma(PrefillArgs a) {
 
   // copies: piece i of copying wave w fills physical chunk p = 256 i + 64 w + lane of a
   // tile: key row p / 40, physical chunk p % 40, logical chunk (p % 40) ^ swz(row)
-  auto dma_src = [&](int t0, int i) -> uint32_t {
-    const int p = 256 * i + 64 * wave + lane;
+  // Per lane and piece (fixed for the workgroup): the source as base + token *
+  // stride.  One register packs, for each piece, the key row inside the tile
+  // (5 bits) and whether the chunk lies in k^R (1 bit); the token is below
+  // 2^24 (the workspace is below 4 GiB), so the product is a 24-bit multiply.
+  uint32_t cp_meta = 0u, cp_base[kADma];
+#pragma unroll
+  for (int i = 0; i < kADma; ++i) {
+    const int p = 256 * i + 64 * min(wave, kACopyWaves - 1) + lane;
     const int r = p / kAChunks, pc = p - r * kAChunks;
     const int lc = pc ^ swz(r);
-    const int tok = s0 + min(t0 + r, Lb - 1);
-    const uint32_t kv = (uint32_t)tok * a.H + h;
-    if (lc < 16) return kv * (kDnP * 2) + 16 * lc;
-    if (lc < 32) return a.v_off + kv * (kDnP * 2) + 16 * (lc - 16);
-    return a.r_off + (uint32_t)tok * (kDrP * 2) + 16 * (lc - 32);
+    const bool isr = lc >= 32;
+    cp_meta |= (uint32_t)(r | (isr ? 32 : 0)) << (6 * i);
+    cp_base[i] = isr ? a.r_off + 16 * (lc - 32)
+                     : (lc >= 16 ? a.v_off : 0u) + (uint32_t)h * (kDnP * 2) + 16 * (lc & 15);
+  }
+  const uint32_t kv_stride = (uint32_t)a.H * (kDnP * 2);
+  auto dma_src = [&](int t0, int i) -> uint32_t {
+    const uint32_t mi = cp_meta >> (6 * i);
+    const int tok = min(s0 + t0 + (int)(mi & 31), s0 + Lb - 1);
+    return cp_base[i] + __umul24((uint32_t)tok, (mi & 32) ? (uint32_t)(kDrP * 2) : kv_stride);
   };
   auto dma_to = [&](int t0, uint32_t dst, uint32_t stride, int i) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + stride * i);
     __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_src(t0, i)), "s"(a.ws), "{m0}"(m0)
                      : "memory");
   };
-  auto issue = [&](int sub) {
-    if (!copier) return;
+  auto issue = [&](int sub, auto copy_tag) {
+    if constexpr (!decltype(copy_tag)::value) return;
 #pragma unroll
     for (int i = 0; i < kADma; ++i)
       dma_to(sub * kKT, (uint32_t)(uintptr_t)smem + (sub & (kAStages - 1)) * kATile + wave * 1024, 4096, i);
@@ -300,16 +312,21 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_mfma(PrefillArgs a) {
 
   f32x16 o[kAMB];
   float m = -INFINITY, l = 0.f, m_seen = -INFINITY;
+  // The whole pass loop is instantiated twice, for the waves that issue the
+  // copies and for those that do not, so that neither carries a per-copy
+  // branch; both run the same sequence of barriers.
+  auto passes = [&](auto copy_tag) {
+  constexpr bool kCopy = decltype(copy_tag)::value;
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int mb = 0; mb < kAMB; ++mb) o[mb] = f32x16{};
     l = 0.f;
     m = pass ? m_seen : -INFINITY;
     bool overflow = false;
-    for (int s2 = 0; s2 < min(3, n_sub); ++s2) issue(s2);
+    for (int s2 = 0; s2 < min(3, n_sub); ++s2) issue(s2, copy_tag);
 
     // ---- prologue: tile 0 landed, its scores computed
-    if (copier) vm_wait_a(min(2, n_sub - 1) * kADma);
+    if constexpr (kCopy) vm_wait_a(min(2, n_sub - 1) * kADma);
     block_sync();
     f32x16 sc;
     {
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_mfma(PrefillArgs a) {
       const int t0 = i * kKT;
       const bool nxt = i + 1 < n_sub;
       if (nxt) {
-        if (copier) vm_wait_a(i + 2 < n_sub ? kADma : 0);
+        if constexpr (kCopy) vm_wait_a(i + 2 < n_sub ? kADma : 0);
         block_sync();  // tile i+1 landed; every wave is past PV(i-1)
       }
       // tile i+3 is copied during the score loop below (a re-read of the
@@ -423,7 +440,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_mfma(PrefillArgs a) {
           if (ks == 0) mfma_v0(sn, kop[0], q[0]);
           else mfma_v(sn, kop[ks % 4], q[ks]);
           piece(ks);
-          if (copier && (ks & 1) && (ks >> 1) < kADma) dma_to(copy_t0, copy_dst, copy_stride, ks >> 1);
+          if constexpr (kCopy) {
+            if ((ks & 1) && (ks >> 1) < kADma) dma_to(copy_t0, copy_dst, copy_stride, ks >> 1);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -483,7 +502,10 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_mfma(PrefillArgs a) {
     if (red_flag == 0) break;
     block_sync();
   }
-  if (copier) vm_wait<0>();  // the sink copies of the last tiles
+  if constexpr (kCopy) vm_wait<0>();  // the sink copies of the last tiles
+  };
+  if (copier) passes(std::true_type{});
+  else passes(std::false_type{});
 
   if (row_ok) {
     const size_t tq = (size_t)(s0 + qrow) * a.H + h;
