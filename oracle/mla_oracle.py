@@ -51,6 +51,11 @@ __all__ = [
     "cache_rows_reference",
     "cache_append_reference",
     "prefill_reference",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "fp8_cache_values",
+    "cache_append_fp8_reference",
 ]
 
 
@@ -350,3 +355,78 @@ def prefill_reference(q_nope, q_rope, c_kv, k_rope, cu_seqlens, w_uk, w_uv, scal
                 u[t, h] = p[0] @ vals[:n_vis]
                 lse[t, h] = lse_t[0]
     return u, lse
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) latent cache.  "Deconstructing DeepSeek V4 Pro", Practical
+# Deployment (quantization strategies): the compressed latent tolerates FP8
+# (E4M3/E5M2), which brings a token's cached row below a kilobyte; "DeepSeek-V3
+# MLA: Multi-Head Latent Attention Guide", Core Architecture: the 576 cached
+# values per token are kept in fp8 or bf16.  The pages name the format only;
+# the readings taken here are: the whole row [c^KV | k^R] is E4M3 (576 bytes),
+# one float scale per cache (a stored code q stands for scale * value(q)), and
+# encoding rounds to the nearest code with ties to the even code, saturating
+# at +-448 so that a finite latent never becomes NaN.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """Values (float64) of E4M3 codes, from the format's definition (OCP 8-bit
+    floating point, E4M3): bit 7 is the sign, bits 6..3 the exponent with bias
+    7, bits 2..0 the mantissa.  Exponent field 0 holds the subnormals
+    m/8 * 2^-6; otherwise the value is (1 + m/8) * 2^(e-7).  The code with all
+    six exponent and mantissa bits set is NaN; there are no infinities, so the
+    largest magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    sign = np.where((c & 0x80) != 0, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def e4m3_encode(x):
+    """E4M3 code (uint8) nearest to x, ties to the even code, saturating:
+    magnitudes of 448 and above give the code of +-448.  -0.0 keeps its sign
+    bit; NaN gives the NaN code 0x7F.  Written as a nearest-neighbour search
+    over the 127 non-negative finite values."""
+    x = np.asarray(x, dtype=np.float64)
+    table = e4m3_decode(np.arange(0x7F))  # codes 0x00..0x7E: 0 .. 448, increasing
+    a = np.minimum(np.abs(np.where(np.isnan(x), 0.0, x)), E4M3_MAX)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, len(table) - 1)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = pick | np.where(np.signbit(x), 0x80, 0)
+    return np.where(np.isnan(x), 0x7F, code).astype(np.uint8)
+
+
+def fp8_cache_values(codes, kv_scale):
+    """The latent cache an E4M3 code cache stands for: kv_scale * value(code),
+    float64, same shape.  Decoding over it is mla_decode_reference unchanged."""
+    return float(kv_scale) * e4m3_decode(codes)
+
+
+def cache_append_fp8_reference(codes, block_table, seq_lens, h, w_dkv, w_kr, kv_scale, base=10000.0,
+                               row_dtype=np.float64):
+    """The E4M3 code cache after writing the rows of the q_len new tokens: the
+    row of new token j of sequence b is cache_rows_reference(...) at position
+    seq_lens[b] - q_len + j, divided by kv_scale and encoded with
+    e4m3_encode.  ``row_dtype`` is the precision in which the row value meets
+    the rounding decision (float64 by default; float32 to take the decision in
+    the kernel's precision).  Every other code is left as it was."""
+    out = np.array(codes, dtype=np.uint8, copy=True)
+    h = np.asarray(h, dtype=np.float64)
+    B, Lq, _ = h.shape
+    bs = out.shape[1]
+    for b in range(B):
+        for j in range(Lq):
+            pos = int(seq_lens[b]) - Lq + j  # position of new token j
+            if pos < 0:
+                raise ValueError("a sequence is shorter than q_len")
+            row = cache_rows_reference(h[b, j], w_dkv, w_kr, pos, base).astype(row_dtype)
+            out[int(block_table[b, pos // bs]), pos % bs, :] = e4m3_encode(row / row_dtype(kv_scale))
+    return out

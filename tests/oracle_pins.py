@@ -22,7 +22,12 @@ Independent routes used here:
   * for the prefill: the absorbed algebra per query token, torch's float64
     scaled_dot_product_attention with is_causal, scalar loops, the decode
     oracle on every prefix (a causal prefill row is a decode step), the key
-    permutation invariance of the unmasked form, and the one-key closed form.
+    permutation invariance of the unmasked form, and the one-key closed form;
+  * for the FP8 (E4M3) cache: torch's float8_e4m3fn conversions (a library
+    implementation of the same format), values the format's definition fixes
+    (1, 2, 1.5, 448, the smallest normal and subnormal, -0), a pure-Python
+    nearest-code search over all finite codes, and the float cache append
+    rounded through torch.
 """
 from __future__ import annotations
 
@@ -502,6 +507,107 @@ def pin_prefill_select(orc, seed=25):
     assert np.isnan(us[1, 0]).all()
 
 
+# ------------------------------------------------------------------ FP8 (E4M3) cache
+
+def pin_e4m3_decode_library(orc, seed=30):
+    """Every one of the 256 codes decodes to what torch's float8_e4m3fn dtype gives."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert int(np.isnan(got).sum()) == 2  # 0x7F and 0xFF only
+
+
+def pin_e4m3_known_values(orc, seed=31):
+    """Values the format's definition fixes (sign 1 bit, exponent 4 bits with bias 7, mantissa 3 bits)."""
+    table = {0x38: 1.0, 0x40: 2.0, 0x3C: 1.5, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9,
+             0x07: 7.0 * 2.0 ** -9, 0x00: 0.0, 0xB8: -1.0, 0xFE: -448.0, 0x30: 0.5, 0x77: 240.0}
+    for code, val in table.items():
+        assert orc.e4m3_decode(np.array([code]))[0] == val, hex(code)
+    z = orc.e4m3_decode(np.array([0x80]))[0]
+    assert z == 0.0 and np.signbit(z)
+    assert orc.E4M3_MAX == 448.0
+
+
+def _e4m3_nearest_bruteforce(x, values):
+    """Nearest finite code by scanning every code, ties to the even code, saturating, -0 and NaN kept."""
+    if math.isnan(x):
+        return 0x7F
+    sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+    a = min(abs(x), 448.0)
+    best, best_d = None, None
+    for code in range(0x7F):
+        d = abs(a - values[code])
+        if best is None or d < best_d or (d == best_d and code % 2 == 0):
+            best, best_d = code, d
+    return best | sign
+
+
+def pin_e4m3_encode_bruteforce(orc, seed=32):
+    """Encoding equals a scalar nearest-code search, on random values, exact midpoints, tiny and huge values."""
+    rng = np.random.default_rng(seed)
+    values = [float(v) for v in torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn)
+              .to(torch.float64).numpy()]
+    xs = list(rng.standard_normal(300) * 40.0) + list(rng.standard_normal(100) * 0.01)
+    for c in range(0x7E):  # midpoints of neighbouring codes (ties) and points just off them
+        mid = 0.5 * (values[c] + values[c + 1])
+        xs += [mid, -mid, math.nextafter(mid, 0.0), math.nextafter(mid, 1e9)]
+    xs += [448.0, 449.0, 463.9, 464.0, 500.0, 1e9, -1e9, 0.0, -0.0, 1e-30, -1e-30, float("nan")]
+    got = orc.e4m3_encode(np.array(xs))
+    for x, g in zip(xs, got):
+        assert int(g) == _e4m3_nearest_bruteforce(x, values), (x, int(g))
+
+
+def pin_e4m3_encode_library(orc, seed=33):
+    """Inside the finite range the encoding equals torch's round-to-nearest-even cast to float8_e4m3fn."""
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([rng.standard_normal(20000) * 60.0, rng.standard_normal(5000) * 1e-3])
+    x = x[np.abs(x) < 440.0]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.e4m3_encode(x), ref)
+
+
+def pin_fp8_cache_values(orc, seed=34):
+    """The cache an FP8 code cache stands for is scale * the library-decoded value of each code."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(3, 4, 5)).astype(np.uint8)
+    codes[codes == 0x7F] = 0x7E
+    codes[codes == 0xFF] = 0xFE
+    scale = 0.0123
+    ref = scale * torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    _close(orc.fp8_cache_values(codes, scale), ref)
+
+
+def pin_cache_append_fp8(orc, seed=35):
+    """The FP8 append writes, into exactly the new tokens' slots, the float append's rows divided by the
+    scale and rounded by torch's float8_e4m3fn cast (within the finite range)."""
+    rng = np.random.default_rng(seed)
+    B, Lq, d, d_c, d_r, bs, NB = 2, 2, 12, 6, 4, 4, 7
+    h = rng.standard_normal((B, Lq, d))
+    w_dkv = rng.standard_normal((d_c, d)) / math.sqrt(d)
+    w_kr = rng.standard_normal((d_r, d)) / math.sqrt(d)
+    table = np.array([[3, 0, 5], [6, 1, 2]])
+    lens = np.array([6, 9])
+    codes = rng.integers(0, 0x7E, size=(NB, bs, d_c + d_r)).astype(np.uint8)
+    scale = 0.037
+    got = orc.cache_append_fp8_reference(codes, table, lens, h, w_dkv, w_kr, scale)
+    ref_float = orc.cache_append_reference(np.zeros((NB, bs, d_c + d_r)), table, lens, h, w_dkv, w_kr)
+    written = np.zeros((NB, bs), dtype=bool)
+    for b in range(B):
+        for j in range(Lq):
+            t = int(lens[b]) - Lq + j
+            blk, slot = int(table[b, t // bs]), t % bs
+            written[blk, slot] = True
+            row = ref_float[blk, slot] / scale
+            assert np.abs(row).max() < 440.0
+            want = torch.from_numpy(row).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(got[blk, slot], want)
+    assert np.array_equal(got[~written], codes[~written])
+
+
 ALL_PINS = [
     pin_absorbed_route,
     pin_library_sdpa,
@@ -525,4 +631,10 @@ ALL_PINS = [
     pin_prefill_matches_decode,
     pin_prefill_key_permutation,
     pin_prefill_select,
+    pin_e4m3_decode_library,
+    pin_e4m3_known_values,
+    pin_e4m3_encode_bruteforce,
+    pin_e4m3_encode_library,
+    pin_fp8_cache_values,
+    pin_cache_append_fp8,
 ]

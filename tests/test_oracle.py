@@ -106,6 +106,18 @@ MUTATIONS = {
     "prefill_missing_scale": ("sc = scale * (keys[:n_vis] @ q)", "sc = keys[:n_vis] @ q"),
     "prefill_rope_query_dropped": ("q = np.concatenate([q_nope[t, h], q_rope[t, h]])\n                n_vis",
                                    "q = np.concatenate([q_nope[t, h], 0.0 * q_rope[t, h]])\n                n_vis"),
+    "e4m3_bias_8": ("np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
+    "e4m3_subnormal_scale": ("m / 8.0 * 2.0 ** -6", "m / 8.0 * 2.0 ** -7"),
+    "e4m3_nan_whole_top_binade": ("np.where((e == 15) & (m == 7), np.nan, val)", "np.where(e == 15, np.nan, val)"),
+    "e4m3_ties_up": ("np.where(lo % 2 == 0, lo, hi)", "hi"),
+    "e4m3_sign_dropped": ("code = pick | np.where(np.signbit(x), 0x80, 0)", "code = pick"),
+    "e4m3_nan_on_overflow": ("return np.where(np.isnan(x), 0x7F, code).astype(np.uint8)",
+                             "return np.where(np.isnan(x) | (np.abs(x) >= 464), 0x7F, code).astype(np.uint8)"),
+    "fp8_scale_inverted": ("return float(kv_scale) * e4m3_decode(codes)", "return e4m3_decode(codes) / float(kv_scale)"),
+    "append_fp8_scale_multiplied": ("e4m3_encode(row / row_dtype(kv_scale))", "e4m3_encode(row * row_dtype(kv_scale))"),
+    "append_fp8_wrong_slot": ("out[int(block_table[b, pos // bs]), pos % bs, :] = e4m3_encode(",
+                              "out[int(block_table[b, pos // bs]), (pos + 1) % bs, :] = e4m3_encode("),
+    "append_fp8_position_off_by_one": ("pos = int(seq_lens[b]) - Lq + j  #", "pos = int(seq_lens[b]) - Lq + j - 1  #"),
 }
 
 
