@@ -147,6 +147,38 @@ int mla_decode_planned(const mla_dims* dims, const void* q_cat, const void* kv_c
                        float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
                        float* o_partial, float* lse_partial, void* stream);
 
+/* ---- FP8 latent cache ---------------------------------------------------
+ * The latent cache in FP8 ("Deconstructing DeepSeek V4 Pro", Practical
+ * Deployment: the compressed latent tolerates FP8 E4M3 quantization and the
+ * cached row drops below a kilobyte; "DeepSeek-V3 MLA: Multi-Head Latent
+ * Attention Guide", Core Architecture: the 576 cached values per token in
+ * fp8 or bf16).  kv_cache is [NB, block_size, d_c + d_rope] uint8: every
+ * element of the row [c^KV | k^R] is an OCP E4M3 code (bit 7 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; no infinities; all six low bits set is
+ * NaN; largest magnitude 448), and a code stands for kv_scale times its value
+ * (one float scale for the whole cache, finite and > 0).  The result is that
+ * of mla_decode on the cache of those values: E4M3 values are exact in bf16
+ * and float32, so the products see exactly the cached values (bf16 q_cat
+ * storage uses the matrix-core kernel when mla_decode would, the portable
+ * kernel otherwise).  o_partial/lse_partial are as for mla_decode (o_s in
+ * value units, the scale applied).  Rows a sequence never reaches may hold
+ * any code, NaN included.  The planner weighs a piece's fixed cost against
+ * the halved row bytes, so plan FP8 calls with mla_decode_plan_fp8 and size
+ * them with mla_decode_num_splits_fp8 (the schedule format is the same, so a
+ * schedule from either planner serves either attention call with the same
+ * num_splits); the workspace is as for mla_decode. */
+int mla_decode_num_splits_fp8(const mla_dims* dims, int32_t max_seq_len, int64_t total_tokens,
+                              int32_t* num_splits);
+int mla_decode_plan_fp8(const mla_dims* dims, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+int mla_decode_planned_fp8(const mla_dims* dims, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
+                           const int32_t* block_table, float softmax_scale, int32_t num_splits,
+                           const void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial,
+                           void* stream);
+int mla_decode_fp8(const mla_dims* dims, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
+                   const int32_t* block_table, const int32_t* seq_lens, float softmax_scale, int32_t num_splits,
+                   void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream);
+
 /* Log-sum-exp merge of the splits (exact rewrite of one softmax over the
  * union of the splits' keys):
  *   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s

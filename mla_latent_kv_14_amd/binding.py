@@ -58,6 +58,10 @@ def load() -> ctypes.CDLL:
         "mla_decode": [D, P, P, P, P, F32, I32, P, SZ, P, P, P],
         "mla_decode_plan": [D, P, I32, P, SZ, P],
         "mla_decode_planned": [D, P, P, P, F32, I32, P, SZ, P, P, P],
+        "mla_decode_num_splits_fp8": [D, I32, I64, ctypes.POINTER(I32)],
+        "mla_decode_plan_fp8": [D, P, I32, P, SZ, P],
+        "mla_decode_planned_fp8": [D, P, P, F32, P, F32, I32, P, SZ, P, P, P],
+        "mla_decode_fp8": [D, P, P, F32, P, P, F32, I32, P, SZ, P, P, P],
         "mla_combine": [D, I32, P, P, P, P, P],
         "mla_absorb_out": [D, P, P, P, P],
         "mla_combine_absorb_out": [D, I32, P, P, P, P, P, P, P],
@@ -188,6 +192,57 @@ def mla_decode_planned(dims, q_cat, kv_cache, block_table, softmax_scale, num_sp
         _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D),
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq), float(softmax_scale),
         int(num_splits), ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
+
+
+# ---- FP8 (E4M3) latent cache: kv_cache is a uint8 tensor of codes standing for kv_scale * value
+
+def mla_decode_num_splits_fp8(dims, max_seq_len: int, total_tokens: int) -> int:
+    out = ctypes.c_int32(0)
+    _check("mla_decode_num_splits_fp8", load().mla_decode_num_splits_fp8(ctypes.byref(dims), int(max_seq_len),
+                                                                         int(total_tokens), ctypes.byref(out)))
+    return out.value
+
+
+def mla_decode_plan_fp8(dims, seq_lens, num_splits, workspace, stream=None):
+    d = dims
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_decode_plan_fp8", load().mla_decode_plan_fp8(
+        ctypes.byref(d), _ptr(seq_lens, "seq_lens", torch.int32, d.batch), int(num_splits),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_decode_planned_fp8(dims, q_cat, kv_cache, kv_scale, block_table, softmax_scale, num_splits, workspace,
+                           o_partial, lse_partial, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    D = d.d_c + d.d_rope
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_decode_planned_fp8", load().mla_decode_planned_fp8(
+        ctypes.byref(d), _ptr(q_cat, "q_cat", st, rows * D),
+        _ptr(kv_cache, "kv_cache", torch.uint8, d.num_blocks * d.block_size * D), float(kv_scale),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq), float(softmax_scale),
+        int(num_splits), ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
+
+
+def mla_decode_fp8(dims, q_cat, kv_cache, kv_scale, block_table, seq_lens, softmax_scale, num_splits, workspace,
+                   o_partial, lse_partial, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    D = d.d_c + d.d_rope
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check("mla_decode_fp8", load().mla_decode_fp8(
+        ctypes.byref(d), _ptr(q_cat, "q_cat", st, rows * D),
+        _ptr(kv_cache, "kv_cache", torch.uint8, d.num_blocks * d.block_size * D), float(kv_scale),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch), float(softmax_scale), int(num_splits),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
         _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
 

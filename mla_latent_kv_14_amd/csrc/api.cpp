@@ -81,7 +81,7 @@ struct DecodeShape {
   int ov;         // overhead tiles the planner charges per sequence
 };
 
-int decode_shape(const mla_dims& d, DecodeShape* out) {
+int decode_shape(const mla_dims& d, bool fp8, DecodeShape* out) {
   int cus = 0;
   int st = device_cus(&cus);
   if (st != MLA_OK) return st;
@@ -103,10 +103,13 @@ int decode_shape(const mla_dims& d, DecodeShape* out) {
       // R * (1152 B of queries + 2048 B of partial result) at 0.9 times the
       // cost of streaming as many bytes of cache, in 64-row tiles of 73728 B:
       //   ov = round(1.5 + R * 3200 * 0.9 / 73728)   (7 at R = 128, 3 at R = 32)
+      // An FP8 tile is half the bytes, so the same fixed cost is twice the
+      // tiles (12 at R = 128) and the smallest worthwhile range doubles.
       const int R = d.q_len * d.num_heads;
+      const int64_t tile_bytes = fp8 ? 36864 : 73728;
       out->grid = cus;
-      out->min_chunk = (R > 32) ? 4 : 2;
-      const int ov = (int)(((int64_t)R * 2880 + 147456) / 73728);
+      out->min_chunk = ((R > 32) ? 4 : 2) * (fp8 ? 2 : 1);
+      const int ov = (int)(((int64_t)R * 2880 + 2 * tile_bytes) / tile_bytes);
       out->ov = ov < 1 ? 1 : ov;
       return MLA_OK;
     }
@@ -150,12 +153,14 @@ int mla_decode_workspace_bytes(const mla_dims* d, int32_t num_splits, size_t* by
   return MLA_OK;
 }
 
-int mla_decode_num_splits(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits) {
+namespace {
+
+int num_splits_impl(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits, bool fp8) {
   int st = check_dims(d);
   if (st != MLA_OK) return st;
   if (num_splits == nullptr || max_seq_len <= 0 || total_tokens < max_seq_len) return MLA_ERR_INVALID_ARG;
   DecodeShape sh;
-  st = decode_shape(*d, &sh);
+  st = decode_shape(*d, fp8, &sh);
   if (st != MLA_OK) return st;
   const int64_t tile = 64;
   const int64_t total_tiles = (total_tokens + tile - 1) / tile;  // lower bound of the planner's sum, so S is never too small
@@ -169,8 +174,6 @@ int mla_decode_num_splits(const mla_dims* d, int32_t max_seq_len, int64_t total_
   return MLA_OK;
 }
 
-namespace {
-
 int check_decode_common(const mla_dims* d, int32_t num_splits, const void* workspace, size_t workspace_bytes) {
   int st = check_dims(d);
   if (st != MLA_OK) return st;
@@ -182,12 +185,14 @@ int check_decode_common(const mla_dims* d, int32_t num_splits, const void* works
   return MLA_OK;
 }
 
+bool positive_finite(float x) { return x > 0.f && x == x && x != INFINITY; }
+
 int check_attention_args(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
-                         float softmax_scale, float* o_partial, float* lse_partial) {
+                         float softmax_scale, float* o_partial, float* lse_partial, bool fp8, float kv_scale) {
   if (!ptr_ok(q_cat) || !ptr_ok(kv_cache) || !ptr_ok(block_table) || !ptr_ok(o_partial) || !ptr_ok(lse_partial))
     return MLA_ERR_INVALID_ARG;
-  if (!(softmax_scale > 0.f) || softmax_scale != softmax_scale || softmax_scale == INFINITY)
-    return MLA_ERR_INVALID_ARG;
+  if (!positive_finite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (fp8 && !positive_finite(kv_scale)) return MLA_ERR_INVALID_ARG;
   (void)d;
   return MLA_OK;
 }
@@ -199,62 +204,110 @@ hipError_t enqueue_plan(const mla_dims& d, const int32_t* seq_lens, int32_t num_
 
 hipError_t enqueue_attention(const mla_dims& d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                              float softmax_scale, int32_t num_splits, const void* workspace, const DecodeShape& sh,
-                             float* o_partial, float* lse_partial, hipStream_t s) {
+                             float* o_partial, float* lse_partial, hipStream_t s, bool fp8, float kv_scale) {
   const int32_t* ws = static_cast<const int32_t*>(workspace);
+  const float kv = fp8 ? kv_scale : 1.f;
   switch (pick_decode(d)) {
     case DecodeKind::Generic:
       return mla::launch_decode_generic(d, q_cat, kv_cache, block_table, ws, softmax_scale, num_splits, sh.grid,
-                                        o_partial, lse_partial, s);
+                                        o_partial, lse_partial, s, fp8, kv);
     case DecodeKind::Mfma:
       return mla::launch_decode_mfma(d, q_cat, kv_cache, block_table, ws, softmax_scale, num_splits, sh.grid,
-                                     o_partial, lse_partial, s);
+                                     o_partial, lse_partial, s, fp8, kv);
   }
   return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-int mla_decode_plan(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int plan_impl(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+              size_t workspace_bytes, void* stream, bool fp8) {
   int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
   if (!ptr_ok(seq_lens)) return MLA_ERR_INVALID_ARG;
   DecodeShape sh;
-  st = decode_shape(*d, &sh);
+  st = decode_shape(*d, fp8, &sh);
   if (st != MLA_OK) return st;
   return to_status(enqueue_plan(*d, seq_lens, num_splits, workspace, sh, (hipStream_t)stream));
 }
 
-int mla_decode_planned(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
-                       float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
-                       float* o_partial, float* lse_partial, void* stream) {
+int planned_impl(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                 float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                 float* o_partial, float* lse_partial, void* stream, bool fp8, float kv_scale) {
   int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
-  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial);
+  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial, fp8, kv_scale);
   if (st != MLA_OK) return st;
   DecodeShape sh;
-  st = decode_shape(*d, &sh);
+  st = decode_shape(*d, fp8, &sh);
   if (st != MLA_OK) return st;
   return to_status(enqueue_attention(*d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, sh,
-                                     o_partial, lse_partial, (hipStream_t)stream));
+                                     o_partial, lse_partial, (hipStream_t)stream, fp8, kv_scale));
 }
 
-int mla_decode(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
-               const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
-               size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+int decode_impl(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
+                size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream, bool fp8,
+                float kv_scale) {
   int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
   if (!ptr_ok(seq_lens)) return MLA_ERR_INVALID_ARG;
-  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial);
+  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial, fp8, kv_scale);
   if (st != MLA_OK) return st;
   DecodeShape sh;
-  st = decode_shape(*d, &sh);
+  st = decode_shape(*d, fp8, &sh);
   if (st != MLA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = enqueue_plan(*d, seq_lens, num_splits, workspace, sh, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
   return to_status(enqueue_attention(*d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, sh,
-                                     o_partial, lse_partial, s));
+                                     o_partial, lse_partial, s, fp8, kv_scale));
+}
+
+}  // namespace
+
+int mla_decode_num_splits(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits) {
+  return num_splits_impl(d, max_seq_len, total_tokens, num_splits, false);
+}
+
+int mla_decode_plan(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return plan_impl(d, seq_lens, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+int mla_decode_planned(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                       float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                       float* o_partial, float* lse_partial, void* stream) {
+  return planned_impl(d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, workspace_bytes,
+                      o_partial, lse_partial, stream, false, 1.f);
+}
+
+int mla_decode(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+               const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+  return decode_impl(d, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
+                     workspace_bytes, o_partial, lse_partial, stream, false, 1.f);
+}
+
+int mla_decode_num_splits_fp8(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits) {
+  return num_splits_impl(d, max_seq_len, total_tokens, num_splits, true);
+}
+
+int mla_decode_plan_fp8(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return plan_impl(d, seq_lens, num_splits, workspace, workspace_bytes, stream, true);
+}
+
+int mla_decode_planned_fp8(const mla_dims* d, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
+                           const int32_t* block_table, float softmax_scale, int32_t num_splits, const void* workspace,
+                           size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+  return planned_impl(d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, workspace_bytes,
+                      o_partial, lse_partial, stream, true, kv_scale);
+}
+
+int mla_decode_fp8(const mla_dims* d, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
+                   const int32_t* block_table, const int32_t* seq_lens, float softmax_scale, int32_t num_splits,
+                   void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+  return decode_impl(d, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
+                     workspace_bytes, o_partial, lse_partial, stream, true, kv_scale);
 }
 
 int mla_combine(const mla_dims* d, int32_t num_splits, const float* o_partial, const float* lse_partial,

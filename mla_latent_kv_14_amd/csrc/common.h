@@ -44,6 +44,7 @@ struct DecodeArgs {
   float* lse_part;
   float scale;
   int32_t B, Lq, H, d_c, d_rope, block_size, max_blocks, num_blocks, splits;
+  float kv_scale;  // FP8 cache: a stored code stands for kv_scale * its value (1 otherwise)
 };
 
 // ---- float <-> storage conversions -------------------------------------------------

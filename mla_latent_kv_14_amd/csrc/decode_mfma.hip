@@ -36,6 +36,15 @@
 // chunk c sits at physical chunk c ^ g(r), g(r) = ((r>>1)&1)<<2 | (r>>2)&3,
 // which spreads both the score reads (16 rows, same chunk) and the transpose
 // reads (4 rows x 4 chunks) over all 64 banks.
+//
+// FP8 cache (E4M3 codes, one scale per cache; "Deconstructing DeepSeek V4
+// Pro", Practical Deployment: the latent tolerates FP8): a 32-token sub-tile
+// is 18 KiB of contiguous codes, copied HBM -> LDS by the same copy engine
+// into a ring of four.  When sub-tile i+1 has landed, the four waves convert
+// it into one of two bf16 sub-tile buffers of the layout above (E4M3 values
+// are exact in bf16, so the matrix products see exactly the cached values),
+// zeroing rows past the range, and the bf16 code path runs unchanged.  The
+// scale multiplies the softmax scale and the partial result.
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -61,15 +70,24 @@ constexpr float kHeadroom = 64.0f;  // log2 units a score may exceed the referen
 // LDS operand ring depth of the score and latent-sum loops (reads issued this
 // many steps ahead of their MFMA; deeper rings measured slower)
 constexpr int kOperandAhead = 4;
+// FP8 cache: 576-byte rows, an 18 KiB sub-tile copied in 18 pieces of 1 KiB
+// (five per wave; the last two pieces of waves 2 and 3 go to the sink)
+constexpr int kF8Row = kD;                       // 576
+constexpr int kF8Sub = kSub * kF8Row;            // 18432
+constexpr int kF8Pieces = kF8Sub / 1024;         // 18
+constexpr int kF8DmaPerWave = 5;
+constexpr int kF8Chunks = kF8Sub / 16;           // 1152 16-byte chunks per sub-tile
 
 // byte offset of (row, logical 16-B chunk) inside a sub-tile buffer
 __device__ __forceinline__ int tile_off(int r, int c) { return (r * kChunks + (c ^ swz(r))) * 16; }
 
-__device__ __forceinline__ void vm_wait_n(int n) {  // n in {0, 9, 18}
-  switch (n) {
+// wait until at most `tiles` sub-tiles of N copies each are still in flight
+template <int N>
+__device__ __forceinline__ void vm_wait_tiles(int tiles) {  // tiles in {0, 1, 2}
+  switch (tiles) {
     case 0: vm_wait<0>(); break;
-    case 9: vm_wait<9>(); break;
-    default: vm_wait<18>(); break;
+    case 1: vm_wait<N>(); break;
+    default: vm_wait<2 * N>(); break;
   }
 }
 
@@ -86,14 +104,18 @@ __device__ __forceinline__ void vm_wait_n(int n) {  // n in {0, 9, 18}
 
 // The read-only inputs come as separate __restrict__ arguments so that the
 // compiler may read the schedule through the scalar cache.
-template <int RG>
+template <int RG, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, const int32_t* __restrict__ ws,
                                                                    const int32_t* __restrict__ table,
                                                                    const uint16_t* __restrict__ qc,
                                                                    const uint8_t* __restrict__ cache) {
   constexpr int CG = 4 / RG;   // waves sharing one group of 32 rows (split over O columns)
   constexpr int MB = 16 / CG;  // 32-column blocks of O per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kSubBytes];
+  // bf16 sub-tile buffers: the copy ring itself, or (FP8) two conversion
+  // targets followed by the ring of FP8 sub-tiles
+  constexpr int kBufs = F8 ? 2 : kStages;
+  constexpr int kDmaN = F8 ? kF8DmaPerWave : kDmaPerWave;  // copies per wave per sub-tile
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * kSubBytes + (F8 ? kStages * kF8Sub : 0)];
   // sink for the copies issued when there is no sub-tile left to fetch (so
   // that the score loop carries no per-step condition); never read
   __shared__ __attribute__((aligned(1024))) uint8_t sink[kThreads / 64 * 1024];
@@ -154,9 +176,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   const int q_lane = wave * 64 + lane;
   auto dma_src = [&](int i) {
     const int q = q_lane + 256 * i;
-    const int r = (q * 1821) >> 17;  // q / 72 for 0 <= q < 2304
-    const int pc = q - r * kChunks;
-    return r * kRowBytes + ((pc ^ swz(r)) << 4);
+    if constexpr (F8) {
+      // an FP8 sub-tile is contiguous in the cache and in its ring stage;
+      // pieces past the 18th re-read the start of the sub-tile (into the sink)
+      return (q < kF8Chunks ? q : q - kF8Chunks) << 4;
+    } else {
+      const int r = (q * 1821) >> 17;  // q / 72 for 0 <= q < 2304
+      const int pc = q - r * kChunks;
+      return r * kRowBytes + ((pc ^ swz(r)) << 4);
+    }
   };
 
   // Block-table window of a segment: lane j holds the physical block of the
@@ -188,23 +216,80 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       const int j = t / a.block_size - j0;
       int blk = (j < 64) ? __builtin_amdgcn_readlane(tv, j) : trow[t / a.block_size];
       blk = min(max(blk, 0), a.num_blocks - 1);
-      return cache + ((size_t)blk * a.block_size + (t % a.block_size)) * kRowBytes;
+      return cache + ((size_t)blk * a.block_size + (t % a.block_size)) * (F8 ? kF8Row : kRowBytes);
     };
     auto dma_to = [&](const uint8_t* base, uint32_t dst, uint32_t stride, int i) {
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + stride * i);
       __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_src(i)), "s"(base), "{m0}"(m0)
                        : "memory");
     };
+    // LDS byte address of the copy destination of sub-tile sub: its ring stage
+    auto stage_addr = [&](int sub) -> uint32_t {
+      if constexpr (F8) return (uint32_t)(uintptr_t)smem + kBufs * kSubBytes + (sub & (kStages - 1)) * kF8Sub;
+      else return (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes;
+    };
+    // piece i of this wave lands at stage + 1 KiB * (wave + 4 i), except the
+    // FP8 pieces past the 18th, which go to the sink
     auto dma = [&](const uint8_t* base, int sub, int i) {
-      dma_to(base, (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes + wave * 1024, 4096, i);
+      const bool to_sink = F8 && wave + 4 * i >= kF8Pieces;  // uniform: a select, not a branch
+      dma_to(base, to_sink ? (uint32_t)(uintptr_t)sink + wave * 1024 : stage_addr(sub) + wave * 1024,
+             to_sink ? 0u : 4096u, i);
     };
     auto issue = [&](int sub) {
       const uint8_t* base = tile_src(sub);
 #pragma unroll
-      for (int i = 0; i < kDmaPerWave; ++i) dma(base, sub, i);
+      for (int i = 0; i < kDmaN; ++i) dma(base, sub, i);
+    };
+    // FP8: convert landed sub-tile sub into bf16 buffer sub & 1 (the layout
+    // of the bf16 path), zeros for rows past the range; then a barrier
+    auto convert = [&](int sub) {
+      if constexpr (F8) {
+        const uint8_t* src = smem + kBufs * kSubBytes + (sub & (kStages - 1)) * kF8Sub;
+        uint8_t* dst = smem + (sub & 1) * kSubBytes;
+        const int valid = seg.tok_end - (seg.tok_begin + sub * kSub);  // rows of real tokens
+        // all reads first, then convert and store (16 codes -> two bf16 chunks)
+        constexpr int kIt = (kF8Chunks + kThreads - 1) / kThreads;  // 5
+        uint4 w[kIt];
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+          const int q2 = tid + kThreads * it;
+          w[it] = (q2 < kF8Chunks) ? *reinterpret_cast<const uint4*>(src + q2 * 16) : make_uint4(0, 0, 0, 0);
+        }
+        // codes 0,1 (low half) and 2,3 (high half) of a word -> two bf16 pairs
+        auto cv_lo = [](uint32_t x) {
+          return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+        };
+        auto cv_hi = [](uint32_t x) {
+          return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+        };
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+          const int q2 = tid + kThreads * it;
+          if (q2 < kF8Chunks) {
+            const int r = (q2 * 1821) >> 16;  // q2 / 36 for 0 <= q2 < 1152
+            const int c8 = q2 - r * 36;
+            const bool keep = r < valid;
+            const uint4 x = w[it];
+            const uint4 lo = make_uint4(keep ? cv_lo(x.x) : 0u, keep ? cv_hi(x.x) : 0u, keep ? cv_lo(x.y) : 0u,
+                                        keep ? cv_hi(x.y) : 0u);
+            const uint4 hi4 = make_uint4(keep ? cv_lo(x.z) : 0u, keep ? cv_hi(x.z) : 0u, keep ? cv_lo(x.w) : 0u,
+                                         keep ? cv_hi(x.w) : 0u);
+            *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8)) = lo;
+            *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8 + 1)) = hi4;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        block_sync();
+      } else {
+        (void)sub;
+      }
     };
     // rows of a sub-tile past the sequence end hold unspecified data: zero them
     auto fix_partial = [&](int sub) {
+      if constexpr (F8) {
+        convert(sub);
+        return;
+      }
       const int t0 = seg.tok_begin + sub * kSub;
       if (t0 + kSub > seg.tok_end) {
         uint8_t* buf = smem + (sub & (kStages - 1)) * kSubBytes;
@@ -231,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       first_seg = false;
     }
 
-    const float qk_scale = a.scale * kLog2e;
+    const float qk_scale = a.scale * (F8 ? a.kv_scale : 1.f) * kLog2e;
     const int lim_row = row_ok ? min(seg.tok_end, L - a.Lq + jq + 1) : 0;
     const int lim_all = min(seg.tok_end, L - a.Lq + 1);
 
@@ -259,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       };
 
       // ---- prologue: sub-tile 0 ready, its scores computed
-      vm_wait_n(min(2, n_sub - 1) * 9);
+      vm_wait_tiles<kDmaN>(min(2, n_sub - 1));
       block_sync();
       fix_partial(0);
       f32x16 sc;
@@ -285,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         const int t0 = seg.tok_begin + i * kSub;
         const bool nxt = i + 1 < n_sub;
         if (nxt) {
-          vm_wait_n(i + 2 < n_sub ? 9 : 0);
+          vm_wait_tiles<kDmaN>(i + 2 < n_sub ? 1 : 0);
           block_sync();  // sub-tile i+1 landed; every wave is past PV(i-1)
           fix_partial(i + 1);
         }
@@ -297,8 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         // below (vmcnt) is the same constant, the sink's copies included.
         const bool copy_on = i + 3 < n_sub;
         const uint8_t* copy_src = tile_src(copy_on ? i + 3 : n_sub - 1);
-        const uint32_t copy_dst = copy_on ? (uint32_t)(uintptr_t)smem + ((i + 3) & (kStages - 1)) * kSubBytes + wave * 1024
-                                          : (uint32_t)(uintptr_t)sink + wave * 1024;
+        const uint32_t copy_dst = copy_on ? stage_addr(i + 3) + wave * 1024 : (uint32_t)(uintptr_t)sink + wave * 1024;
         const uint32_t copy_stride = copy_on ? 4096u : 0u;
 
         // masking of sub-tile i (rare: only where some row's last visible token falls inside)
@@ -376,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         f32x16 sn;
         if (nxt) {
           int kb[4];
-          kbases((i + 1) & (kStages - 1), kb);
+          kbases((i + 1) & (kBufs - 1), kb);
           constexpr int kAhead = kOperandAhead;
           bf16x8 kop[kAhead];
 #pragma unroll
@@ -387,7 +471,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
             if (ks == 0) mfma_v0(sn, kop[0], q[0]);
             else mfma_v(sn, kop[ks % kAhead], q[ks]);
             if (ks < kPieces) piece(ks);
-            if (ks % 4 == 2) dma_to(copy_src, copy_dst, copy_stride, ks / 4);
+            if constexpr (F8) {
+              if (ks % 7 == 3) {
+                const int pc = ks / 7;
+                const bool to_sink = wave + 4 * pc >= kF8Pieces;  // uniform: a select, not a branch
+                dma_to(copy_src, to_sink ? (uint32_t)(uintptr_t)sink + wave * 1024 : copy_dst,
+                       to_sink ? 0u : copy_stride, pc);
+              }
+            } else {
+              if (ks % 4 == 2) dma_to(copy_src, copy_dst, copy_stride, ks / 4);
+            }
             __builtin_amdgcn_sched_barrier(0);
           }
         } else {
@@ -405,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int par = 0; par < 2; ++par) {
-              vb[h][par] = (i & (kStages - 1)) * kSubBytes + vbase(h, par);
+              vb[h][par] = (i & (kBufs - 1)) * kSubBytes + vbase(h, par);
               __asm__ volatile("" : "+v"(vb[h][par]));
             }
           constexpr int kSteps = 2 * MB;
@@ -452,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     if (row_ok) {
       const size_t prow = ((size_t)b * R + n) * S;
       if (l > 0.f) {
-        const float inv = 1.f / l;
+        const float inv = (F8 ? a.kv_scale : 1.f) / l;
         float* op = a.o_part + (prow + seg.split) * kDC;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -487,18 +580,24 @@ bool decode_mfma_supported(const mla_dims& d) {
 
 hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
                               const int32_t* ws, float scale, int splits, int grid, float* o_part, float* lse_part,
-                              hipStream_t stream) {
+                              hipStream_t stream, bool fp8, float kv_scale) {
   DecodeArgs a{q_cat, cache, table, ws, o_part, lse_part, scale, d.batch, d.q_len, d.num_heads, d.d_c, d.d_rope,
-               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits};
+               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale};
   const int R = d.q_len * d.num_heads;
   const uint16_t* qc = static_cast<const uint16_t*>(q_cat);
   const uint8_t* kv = static_cast<const uint8_t*>(cache);
-  if (R == 128)
-    hipLaunchKernelGGL(decode_mfma_kernel<4>, dim3(grid), dim3(kThreads), 0, stream, a, ws, table, qc, kv);
-  else if (R == 64)
-    hipLaunchKernelGGL(decode_mfma_kernel<2>, dim3(grid), dim3(kThreads), 0, stream, a, ws, table, qc, kv);
-  else
-    hipLaunchKernelGGL(decode_mfma_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, a, ws, table, qc, kv);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, a, ws, table, qc, kv);
+  };
+  if (fp8) {
+    if (R == 128) go(decode_mfma_kernel<4, true>);
+    else if (R == 64) go(decode_mfma_kernel<2, true>);
+    else go(decode_mfma_kernel<1, true>);
+  } else {
+    if (R == 128) go(decode_mfma_kernel<4, false>);
+    else if (R == 64) go(decode_mfma_kernel<2, false>);
+    else go(decode_mfma_kernel<1, false>);
+  }
   return hipGetLastError();
 }
 

@@ -3,6 +3,8 @@
 // kernels do not cover (float32 storage, small widths, block sizes that are
 // not a multiple of 32) and a second, independent HIP implementation of
 // every step.  None of them is tuned.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -80,10 +82,22 @@ __global__ __launch_bounds__(kThreads) void absorb_out_generic(const float* __re
 }
 
 // ---------------------------------------------------------------------------------------
+// Cache element loads: the storage type, or (uint8_t) an E4M3 code decoded by
+// the hardware conversion (exact in float32).
+template <typename C> struct CacheLoad {
+  __device__ __forceinline__ static float load(const C* p) { return Storage<C>::load(p); }
+};
+template <> struct CacheLoad<uint8_t> {
+  __device__ __forceinline__ static float load(const uint8_t* p) { return __builtin_amdgcn_cvt_f32_fp8((int)*p, 0); }
+};
+
 // Split-KV decode, one wave per query row (j, h).  grid (groups launched, ceil(Lq*H / 4)).
-// Scores: lane = token.  Weighted sum: lane = latent column.
-template <typename T>
+// Scores: lane = token.  Weighted sum: lane = latent column.  T is the storage
+// type of q_cat, C that of the cache (T, or uint8_t for an FP8 cache whose
+// codes stand for kv_scale times their value).
+template <typename T, typename C>
 __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
+  constexpr bool kF8 = std::is_same<C, uint8_t>::value;
   __shared__ float qs[kThreads / 64][kMaxRow];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int R = a.Lq * a.H;
@@ -93,7 +107,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
   const int D = a.d_c + a.d_rope;
   const int S = a.splits;
   const T* qc = (const T*)a.q_cat;
-  const T* cache = (const T*)a.cache;
+  const C* cache = (const C*)a.cache;
+  const float kv = kF8 ? a.kv_scale : 1.f;
   const int32_t* len = a.ws + kWsHeader + a.B + 1;
 
   if (blockIdx.x == 0 && blockIdx.y == 0) mark_empty_sequences(a, threadIdx.x, blockDim.x);
@@ -128,8 +143,9 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
         blk = min(max(blk, 0), a.num_blocks - 1);
         off = ((size_t)blk * a.block_size + t % a.block_size) * D;
         float dot = 0.f;
-        for (int k = 0; k < D; ++k) dot = fmaf(qs[wave][k], Storage<T>::load(cache + off + k), dot);
+        for (int k = 0; k < D; ++k) dot = fmaf(qs[wave][k], CacheLoad<C>::load(cache + off + k), dot);
         s = dot * a.scale;
+        if (kF8) s *= kv;
       }
       const float m_new = fmaxf(m, wave_max(s));
       const float alpha = expf(m - m_new);
@@ -142,11 +158,11 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
         const float pu = __shfl(p, u, 64);
         const unsigned lo = __shfl((unsigned)(off & 0xffffffffu), u, 64);
         const unsigned hi = __shfl((unsigned)(off >> 32), u, 64);
-        const T* rp = cache + (((size_t)hi << 32) | lo);
+        const C* rp = cache + (((size_t)hi << 32) | lo);
 #pragma unroll
         for (int i = 0; i < kMaxCols / 64; ++i) {
           const int c = lane + 64 * i;
-          if (c < a.d_c) acc[i] = fmaf(pu, Storage<T>::load(rp + c), acc[i]);
+          if (c < a.d_c) acc[i] = fmaf(pu, CacheLoad<C>::load(rp + c), acc[i]);
         }
       }
       m = m_new;
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
 
     const size_t prow = ((size_t)(b * a.Lq + j) * a.H + h) * S;
     if (t_end > seg.tok_begin) {
-      const float inv = 1.f / l;
+      const float inv = kF8 ? kv / l : 1.f / l;
       float* op = a.o_part + (prow + seg.split) * a.d_c;
 #pragma unroll
       for (int i = 0; i < kMaxCols / 64; ++i) {
@@ -239,15 +255,18 @@ hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const vo
 
 hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
                                  const int32_t* ws, float scale, int splits, int grid, float* o_part,
-                                 float* lse_part, hipStream_t stream) {
+                                 float* lse_part, hipStream_t stream, bool fp8, float kv_scale) {
   DecodeArgs a{q_cat, cache, table, ws, o_part, lse_part, scale, d.batch, d.q_len, d.num_heads, d.d_c, d.d_rope,
-               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits};
+               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale};
   const int R = d.q_len * d.num_heads;
   dim3 g(grid, (R + kThreads / 64 - 1) / (kThreads / 64));
-  if (d.dtype == MLA_F32)
-    hipLaunchKernelGGL(decode_generic<float>, g, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_generic<uint16_t>, g, dim3(kThreads), 0, stream, a);
+  if (d.dtype == MLA_F32) {
+    if (fp8) hipLaunchKernelGGL((decode_generic<float, uint8_t>), g, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_generic<float, float>), g, dim3(kThreads), 0, stream, a);
+  } else {
+    if (fp8) hipLaunchKernelGGL((decode_generic<uint16_t, uint8_t>), g, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((decode_generic<uint16_t, uint16_t>), g, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ hipError_t launch_absorb_q_generic(const mla_dims& d, const void* q_nope, const 
                                    void* q_cat, hipStream_t stream);
 hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
                                  const int32_t* ws, float scale, int splits, int grid, float* o_part,
-                                 float* lse_part, hipStream_t stream);
+                                 float* lse_part, hipStream_t stream, bool fp8, float kv_scale);
 int decode_generic_rows_per_group();
 hipError_t launch_combine(const mla_dims& d, int splits, const float* o_part, const float* lse_part, float* o,
                           float* lse, hipStream_t stream);
@@ -26,9 +26,10 @@ hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const vo
 
 // matrix-core decode for bf16, d_c = 512, d_rope = 64 (decode_mfma.hip)
 bool decode_mfma_supported(const mla_dims& d);
+// fp8: the cache holds E4M3 codes standing for kv_scale times their value
 hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
                               const int32_t* ws, float scale, int splits, int grid, float* o_part, float* lse_part,
-                              hipStream_t stream);
+                              hipStream_t stream, bool fp8, float kv_scale);
 
 // matrix-core absorption GEMMs for bf16, d_nope = d_v = 128, d_c = 512 (absorb_mfma.hip)
 bool absorb_mfma_supported(const mla_dims& d);

@@ -29,6 +29,13 @@ hidden states h ~ N(0, 1) of width d_model (7168 for the DeepSeek-V3 shapes,
 the input width of the Guide's MLA topology figure), then W^DKV and W^KR ~
 N(0, 1)/sqrt(d_model) (fan-in d_model), rounded like the rest.
 
+FP8 cache workloads (``cache_dtype="fp8"``) draw exactly the same numbers;
+the cache values are then stored as E4M3 codes of value / kv_scale, clipped
+to +-448 and rounded by torch's float8_e4m3fn cast (round to nearest even),
+so each code stands for kv_scale times its value.  kv_scale = 0.0175 puts
+7.8 standard deviations at the top of the format's range.  Poisoned slots
+hold the NaN code 0x7F ("nan") or the codes of +-448 ("big").
+
 Prefill problems (``make_prefill_problem``, the prefill_* workloads) come
 from ``PCG64([seed, 0x9F11])``: lengths by the workload's distribution, then
 the tokens' latents c ~ N(0, 1), RoPE keys ~ N(0, 1), q_nope, q_rope ~ N(0, 1)
@@ -65,6 +72,8 @@ class Workload:
     lengths: tuple  # ("fixed", (L0, L1, ...)) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
     seed_base: int
     d_model: int = 7168  # hidden width h feeding the cache append
+    cache_dtype: str = "same"  # "same" (the storage type) or "fp8" (E4M3 codes)
+    kv_scale: float = 1.0  # FP8 cache: a code stands for kv_scale * its value
 
     @property
     def row_width(self) -> int:
@@ -76,6 +85,8 @@ class Workload:
         return 1.0 / math.sqrt(self.d_nope + self.d_rope)
 
 
+FP8_KV_SCALE = 0.0175  # 448 * 0.0175 = 7.84: the E4M3 range covers 7.8 sigma of N(0, 1) latents
+
 WORKLOADS = {
     w.name: w
     for w in [
@@ -85,6 +96,15 @@ WORKLOADS = {
         Workload("long128k_bf16", "bf16", 4, 128, 512, 64, 128, 128, 1, 64, ("fixed", (131072,) * 4), 4000),
         Workload("mtp2_lognormal_bf16", "bf16", 128, 16, 512, 64, 128, 128, 2, 64,
                  ("lognormal", 2048, 1.0, 64, 32768), 5000),
+        # FP8 (E4M3) latent cache: the same draws as their bf16 twins
+        Workload("tiny_f32_fp8", "f32", 2, 8, 64, 16, 32, 32, 1, 16, ("fixed", (37, 200)), 1000, 96, "fp8",
+                 FP8_KV_SCALE),
+        Workload("single_4k_fp8", "bf16", 1, 128, 512, 64, 128, 128, 1, 64, ("fixed", (4096,)), 2000, 7168, "fp8",
+                 FP8_KV_SCALE),
+        Workload("batch64_1k8k_fp8", "bf16", 64, 128, 512, 64, 128, 128, 1, 64, ("uniform", 1024, 8192), 3000,
+                 7168, "fp8", FP8_KV_SCALE),
+        Workload("mtp2_lognormal_fp8", "bf16", 128, 16, 512, 64, 128, 128, 2, 64,
+                 ("lognormal", 2048, 1.0, 64, 32768), 5000, 7168, "fp8", FP8_KV_SCALE),
         # prefill (whole sequences as queries; q_len and block_size unused)
         Workload("prefill_tiny_f32", "f32", 3, 4, 64, 16, 32, 32, 1, 16, ("fixed", (5, 1, 70)), 6000, 96),
         Workload("prefill_4x4k_bf16", "bf16", 4, 128, 512, 64, 128, 128, 1, 64, ("fixed", (4096,) * 4), 7000),
@@ -128,8 +148,19 @@ class Problem:
     def total_tokens(self) -> int:
         return int(self.seq_lens.astype(np.int64).sum())
 
+    @property
+    def fp8(self) -> bool:
+        return self.wl.cache_dtype == "fp8"
+
+    @property
+    def kv_scale(self) -> float:
+        return float(self.wl.kv_scale)
+
     def f64(self, name: str) -> np.ndarray:
-        """A stored tensor upcast exactly to float64 (what the oracle consumes)."""
+        """A stored tensor upcast exactly to float64 (what the oracle consumes).
+        An FP8 cache holds codes, not values: the oracle decodes those itself."""
+        if name == "cache" and self.fp8:
+            raise ValueError("the FP8 cache holds E4M3 codes; decode them with the oracle")
         return getattr(self, name).to(torch.float64).numpy()
 
 
@@ -185,7 +216,11 @@ def make_problem(wl: Workload, seed: Optional[int] = None, *, poison: Optional[s
         pos += nblk[b]
 
     D = wl.row_width
-    cache = _store(rng.standard_normal((nb_total, bs, D)), wl.dtype)
+    if wl.cache_dtype == "fp8":
+        vals = np.clip(rng.standard_normal((nb_total, bs, D)) / wl.kv_scale, -448.0, 448.0)
+        cache = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8)
+    else:
+        cache = _store(rng.standard_normal((nb_total, bs, D)), wl.dtype)
     q_nope = _store(rng.standard_normal((wl.batch, wl.q_len, wl.heads, wl.d_nope)), wl.dtype)
     q_rope = _store(rng.standard_normal((wl.batch, wl.q_len, wl.heads, wl.d_rope)), wl.dtype)
     inv = 1.0 / math.sqrt(wl.d_c)
@@ -197,7 +232,16 @@ def make_problem(wl: Workload, seed: Optional[int] = None, *, poison: Optional[s
             tail = int(lens[b]) % bs
             if tail:
                 blk = int(table[b, nblk[b] - 1])
-                if poison == "nan":
+                if wl.cache_dtype == "fp8":
+                    if poison == "nan":
+                        cache[blk, tail:, :] = 0x7F
+                    elif poison == "big":
+                        codes = torch.full((bs - tail, D), 0x7E, dtype=torch.uint8)
+                        codes[1::2] = 0xFE
+                        cache[blk, tail:, :] = codes
+                    else:
+                        raise ValueError(f"unknown poison {poison!r}")
+                elif poison == "nan":
                     cache[blk, tail:, :] = float("nan")
                 elif poison == "big":
                     sign = torch.ones(bs - tail, D)

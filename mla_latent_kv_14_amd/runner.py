@@ -32,11 +32,13 @@ class DecodeRunner:
         self.w_uv = prob.w_uv.to(dev)
         self.block_table = torch.from_numpy(np.ascontiguousarray(prob.block_table)).to(dev)
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(prob.seq_lens)).to(dev)
+        self.fp8 = prob.fp8  # the cache holds E4M3 codes standing for prob.kv_scale * value
         if num_splits is None:
-            num_splits = libmla.mla_decode_num_splits(self.dims, int(prob.seq_lens.max()), prob.total_tokens)
+            sizing = libmla.mla_decode_num_splits_fp8 if self.fp8 else libmla.mla_decode_num_splits
+            num_splits = sizing(self.dims, int(prob.seq_lens.max()), prob.total_tokens)
         self.num_splits = int(num_splits)
         B, Lq, H = wl.batch, wl.q_len, wl.heads
-        st = self.cache.dtype
+        st = torch.float32 if wl.dtype == "f32" else torch.bfloat16
         self.q_cat = torch.empty((B, Lq, H, wl.d_c + wl.d_rope), dtype=st, device=dev)
         ws_bytes = libmla.mla_decode_workspace_bytes(self.dims, self.num_splits)
         self.workspace = torch.empty(ws_bytes // 4, dtype=torch.int32, device=dev)
@@ -65,15 +67,26 @@ class DecodeRunner:
         libmla.mla_absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uk, self.q_cat, stream)
 
     def decode(self, stream=None):
-        libmla.mla_decode(self.dims, self.q_cat, self.cache, self.block_table, self.seq_lens, self.prob.scale,
-                          self.num_splits, self.workspace, self.o_partial, self.lse_partial, stream)
+        if self.fp8:
+            libmla.mla_decode_fp8(self.dims, self.q_cat, self.cache, self.prob.kv_scale, self.block_table,
+                                  self.seq_lens, self.prob.scale, self.num_splits, self.workspace, self.o_partial,
+                                  self.lse_partial, stream)
+        else:
+            libmla.mla_decode(self.dims, self.q_cat, self.cache, self.block_table, self.seq_lens, self.prob.scale,
+                              self.num_splits, self.workspace, self.o_partial, self.lse_partial, stream)
 
     def plan(self, stream=None):
-        libmla.mla_decode_plan(self.dims, self.seq_lens, self.num_splits, self.workspace, stream)
+        planner = libmla.mla_decode_plan_fp8 if self.fp8 else libmla.mla_decode_plan
+        planner(self.dims, self.seq_lens, self.num_splits, self.workspace, stream)
 
     def decode_planned(self, stream=None):
-        libmla.mla_decode_planned(self.dims, self.q_cat, self.cache, self.block_table, self.prob.scale,
-                                  self.num_splits, self.workspace, self.o_partial, self.lse_partial, stream)
+        if self.fp8:
+            libmla.mla_decode_planned_fp8(self.dims, self.q_cat, self.cache, self.prob.kv_scale, self.block_table,
+                                          self.prob.scale, self.num_splits, self.workspace, self.o_partial,
+                                          self.lse_partial, stream)
+        else:
+            libmla.mla_decode_planned(self.dims, self.q_cat, self.cache, self.block_table, self.prob.scale,
+                                      self.num_splits, self.workspace, self.o_partial, self.lse_partial, stream)
 
     def combine(self, stream=None):
         libmla.mla_combine(self.dims, self.num_splits, self.o_partial, self.lse_partial, self.o, self.lse, stream)
