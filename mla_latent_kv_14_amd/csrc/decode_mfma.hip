@@ -40,11 +40,15 @@
 // FP8 cache (E4M3 codes, one scale per cache; "Deconstructing DeepSeek V4
 // Pro", Practical Deployment: the latent tolerates FP8): a 32-token sub-tile
 // is 18 KiB of contiguous codes, copied HBM -> LDS by the same copy engine
-// into a ring of four.  When sub-tile i+1 has landed, the four waves convert
-// it into one of two bf16 sub-tile buffers of the layout above (E4M3 values
-// are exact in bf16, so the matrix products see exactly the cached values),
-// zeroing rows past the range, and the bf16 code path runs unchanged.  The
-// scale multiplies the softmax scale and the partial result.
+// into one of two FP8 stages, and converted by the four waves into one of
+// three bf16 sub-tile buffers of the layout above (E4M3 values are exact in
+// bf16, so the matrix products see exactly the cached values), with rows past
+// the range zeroed; the score, softmax and latent-sum code is that of the
+// bf16 path.  The conversion of sub-tile i+2 runs inside the score loop of
+// sub-tile i+1, one 16-byte chunk of codes at a time, and each wave converts
+// exactly the chunks it copied itself, so once its reads have returned it
+// copies sub-tile i+4 into the same stage without waiting for the others.
+// The scale multiplies the softmax scale and the partial result.
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -113,9 +117,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   constexpr int MB = 16 / CG;  // 32-column blocks of O per wave
   // bf16 sub-tile buffers: the copy ring itself, or (FP8) two conversion
   // targets followed by the ring of FP8 sub-tiles
-  constexpr int kBufs = F8 ? 2 : kStages;
+  constexpr int kBufs = F8 ? 3 : kStages;
+  constexpr int kF8Stages = 2;
   constexpr int kDmaN = F8 ? kF8DmaPerWave : kDmaPerWave;  // copies per wave per sub-tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * kSubBytes + (F8 ? kStages * kF8Sub : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * kSubBytes + (F8 ? kF8Stages * kF8Sub : 0)];
   // sink for the copies issued when there is no sub-tile left to fetch (so
   // that the score loop carries no per-step condition); never read
   __shared__ __attribute__((aligned(1024))) uint8_t sink[kThreads / 64 * 1024];
@@ -177,9 +182,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   auto dma_src = [&](int i) {
     const int q = q_lane + 256 * i;
     if constexpr (F8) {
-      // an FP8 sub-tile is contiguous in the cache and in its ring stage;
-      // pieces past the 18th re-read the start of the sub-tile (into the sink)
-      return (q < kF8Chunks ? q : q - kF8Chunks) << 4;
+      // FP8 sub-tile chunk q (16 codes) is row q & 31, codes 16 (q >> 5) ..;
+      // it lands at stage + 16 q, so a lane always meets the same row.  Pieces
+      // past the 18th re-read the start of the sub-tile (into the sink).
+      const int qq = q < kF8Chunks ? q : q - kF8Chunks;
+      return (qq & 31) * kF8Row + ((qq >> 5) << 4);
     } else {
       const int r = (q * 1821) >> 17;  // q / 72 for 0 <= q < 2304
       const int pc = q - r * kChunks;
@@ -225,8 +232,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     };
     // LDS byte address of the copy destination of sub-tile sub: its ring stage
     auto stage_addr = [&](int sub) -> uint32_t {
-      if constexpr (F8) return (uint32_t)(uintptr_t)smem + kBufs * kSubBytes + (sub & (kStages - 1)) * kF8Sub;
+      if constexpr (F8) return (uint32_t)(uintptr_t)smem + kBufs * kSubBytes + (sub & 1) * kF8Sub;
       else return (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes;
+    };
+    // bf16 buffer of sub-tile t
+    auto buf_of = [&](int t) -> int {
+      if constexpr (F8) return t % 3;
+      else return t & (kStages - 1);
     };
     // piece i of this wave lands at stage + 1 KiB * (wave + 4 i), except the
     // FP8 pieces past the 18th, which go to the sink
@@ -240,13 +252,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
 #pragma unroll
       for (int i = 0; i < kDmaN; ++i) dma(base, sub, i);
     };
-    // FP8: convert landed sub-tile sub into bf16 buffer sub & 1 (the layout
-    // of the bf16 path), zeros for rows past the range; then a barrier
+    // FP8 chunk conversion: the 16 codes of chunk q2 (row q2 & 31, codes
+    // 16 (q2 >> 5) ..) -> the two bf16 chunks of the bf16 layout (rows past
+    // the range are zeroed afterwards by fix_partial)
+    auto cv_lo = [](uint32_t x) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
+    };
+    auto cv_hi = [](uint32_t x) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
+    };
+    auto conv_store = [&](uint8_t* dst, int q2, const uint4& x) {
+      const int r = q2 & 31, c8 = q2 >> 5;
+      const uint4 lo = make_uint4(cv_lo(x.x), cv_hi(x.x), cv_lo(x.y), cv_hi(x.y));
+      const uint4 hi4 = make_uint4(cv_lo(x.z), cv_hi(x.z), cv_lo(x.w), cv_hi(x.w));
+      *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8)) = lo;
+      *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8 + 1)) = hi4;
+    };
+    // FP8: convert landed sub-tile sub into its bf16 buffer in one go (the
+    // first two sub-tiles of a range), then a barrier
     auto convert = [&](int sub) {
       if constexpr (F8) {
-        const uint8_t* src = smem + kBufs * kSubBytes + (sub & (kStages - 1)) * kF8Sub;
-        uint8_t* dst = smem + (sub & 1) * kSubBytes;
-        const int valid = seg.tok_end - (seg.tok_begin + sub * kSub);  // rows of real tokens
+        const uint8_t* src = smem + kBufs * kSubBytes + (sub & 1) * kF8Sub;
+        uint8_t* dst = smem + buf_of(sub) * kSubBytes;
         // all reads first, then convert and store (16 codes -> two bf16 chunks)
         constexpr int kIt = (kF8Chunks + kThreads - 1) / kThreads;  // 5
         uint4 w[kIt];
@@ -255,28 +282,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
           const int q2 = tid + kThreads * it;
           w[it] = (q2 < kF8Chunks) ? *reinterpret_cast<const uint4*>(src + q2 * 16) : make_uint4(0, 0, 0, 0);
         }
-        // codes 0,1 (low half) and 2,3 (high half) of a word -> two bf16 pairs
-        auto cv_lo = [](uint32_t x) {
-          return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
-        };
-        auto cv_hi = [](uint32_t x) {
-          return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
-        };
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
           const int q2 = tid + kThreads * it;
-          if (q2 < kF8Chunks) {
-            const int r = (q2 * 1821) >> 16;  // q2 / 36 for 0 <= q2 < 1152
-            const int c8 = q2 - r * 36;
-            const bool keep = r < valid;
-            const uint4 x = w[it];
-            const uint4 lo = make_uint4(keep ? cv_lo(x.x) : 0u, keep ? cv_hi(x.x) : 0u, keep ? cv_lo(x.y) : 0u,
-                                        keep ? cv_hi(x.y) : 0u);
-            const uint4 hi4 = make_uint4(keep ? cv_lo(x.z) : 0u, keep ? cv_hi(x.z) : 0u, keep ? cv_lo(x.w) : 0u,
-                                         keep ? cv_hi(x.w) : 0u);
-            *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8)) = lo;
-            *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8 + 1)) = hi4;
-          }
+          if (q2 < kF8Chunks) conv_store(dst, q2, w[it]);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         block_sync();
@@ -286,13 +295,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     };
     // rows of a sub-tile past the sequence end hold unspecified data: zero them
     auto fix_partial = [&](int sub) {
-      if constexpr (F8) {
-        convert(sub);
-        return;
-      }
       const int t0 = seg.tok_begin + sub * kSub;
       if (t0 + kSub > seg.tok_end) {
-        uint8_t* buf = smem + (sub & (kStages - 1)) * kSubBytes;
+        uint8_t* buf = smem + buf_of(sub) * kSubBytes;
         for (int q2 = (seg.tok_end - t0) * kChunks + tid; q2 < kSubChunks; q2 += kThreads)
           *reinterpret_cast<uint4*>(buf + q2 * 16) = make_uint4(0, 0, 0, 0);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -329,7 +334,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       l = 0.f;
       m = pass ? m_seen : -INFINITY;
       bool overflow = false;
-      for (int s2 = 0; s2 < min(3, n_sub); ++s2) issue(s2);
+      // copies of the last real sub-tile into the sink keep every wait count
+      // below a constant when there is no sub-tile left to fetch
+      auto issue_or_sink = [&](int sub) {
+        if (sub < n_sub) {
+          issue(sub);
+        } else {
+          const uint8_t* base = tile_src(n_sub - 1);
+#pragma unroll
+          for (int i2 = 0; i2 < kDmaN; ++i2) dma_to(base, (uint32_t)(uintptr_t)sink + wave * 1024, 0, i2);
+        }
+      };
+      if constexpr (F8) {
+        issue_or_sink(0);
+        issue_or_sink(1);
+      } else {
+        for (int s2 = 0; s2 < min(3, n_sub); ++s2) issue(s2);
+      }
 
       // score operand bases for a stage
       auto kbases = [&](int stage, int* kb) {
@@ -344,9 +365,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       };
 
       // ---- prologue: sub-tile 0 ready, its scores computed
-      vm_wait_tiles<kDmaN>(min(2, n_sub - 1));
-      block_sync();
-      fix_partial(0);
+      if constexpr (F8) {
+        // each wave converts the chunks it copied: its own wait suffices
+        vm_wait_tiles<kDmaN>(1);
+        convert(0);  // ends with a barrier
+        fix_partial(0);
+        issue_or_sink(2);
+        vm_wait_tiles<kDmaN>(1);
+        if (n_sub > 1) convert(1);
+        issue_or_sink(3);
+      } else {
+        vm_wait_tiles<kDmaN>(min(2, n_sub - 1));
+        block_sync();
+        fix_partial(0);
+      }
       f32x16 sc;
       {
         int kb[4];
@@ -370,9 +402,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         const int t0 = seg.tok_begin + i * kSub;
         const bool nxt = i + 1 < n_sub;
         if (nxt) {
-          vm_wait_tiles<kDmaN>(i + 2 < n_sub ? 1 : 0);
-          block_sync();  // sub-tile i+1 landed; every wave is past PV(i-1)
-          fix_partial(i + 1);
+          if constexpr (F8) {
+            // this wave's copies of sub-tile i+2 landed (sub-tile i+3 may be in
+            // flight); its conversion writes of sub-tile i+1 are done
+            vm_wait_tiles<kDmaN>(1);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            block_sync();  // bf16 sub-tile i+1 complete; every wave is past PV(i-1)
+            fix_partial(i + 1);
+          } else {
+            vm_wait_tiles<kDmaN>(i + 2 < n_sub ? 1 : 0);
+            block_sync();  // sub-tile i+1 landed; every wave is past PV(i-1)
+            fix_partial(i + 1);
+          }
         }
         // Sub-tile i+3 is copied during the score loop below, one 1 KiB piece
         // every fourth MFMA: a wave can queue only a few copies, and a burst of
@@ -380,10 +421,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         // sub-tile i+3 the copies re-read the last sub-tile (an L2 hit) into
         // the sink, so every step issues the same code and every wait count
         // below (vmcnt) is the same constant, the sink's copies included.
-        const bool copy_on = i + 3 < n_sub;
-        const uint8_t* copy_src = tile_src(copy_on ? i + 3 : n_sub - 1);
-        const uint32_t copy_dst = copy_on ? stage_addr(i + 3) + wave * 1024 : (uint32_t)(uintptr_t)sink + wave * 1024;
+        constexpr int kAheadCopy = F8 ? 4 : 3;  // sub-tile copied during this score loop
+        const bool copy_on = i + kAheadCopy < n_sub;
+        const uint8_t* copy_src = tile_src(copy_on ? i + kAheadCopy : n_sub - 1);
+        const uint32_t copy_dst =
+            copy_on ? stage_addr(i + kAheadCopy) + wave * 1024 : (uint32_t)(uintptr_t)sink + wave * 1024;
         const uint32_t copy_stride = copy_on ? 4096u : 0u;
+        // FP8: sub-tile i+2 is converted during this score loop (when it does
+        // not exist the stage's last sub-tile is converted into the free
+        // buffer instead, which nobody reads); chunk it of this lane is
+        // q2 = tid + 256 it, and the lanes of waves 2 and 3 have no fifth
+        // chunk: theirs is read from the stage start and written to the sink
+        const uint8_t* conv_src = smem + kBufs * kSubBytes + ((i + 2) & 1) * kF8Sub;
+        uint8_t* conv_dst = smem + buf_of(i + 2) * kSubBytes;
+        uint4 conv_x = make_uint4(0, 0, 0, 0);
 
         // masking of sub-tile i (rare: only where some row's last visible token falls inside)
         if (t0 + kSub > lim_all) {
@@ -460,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         f32x16 sn;
         if (nxt) {
           int kb[4];
-          kbases((i + 1) & (kBufs - 1), kb);
+          kbases(buf_of(i + 1), kb);
           constexpr int kAhead = kOperandAhead;
           bf16x8 kop[kAhead];
 #pragma unroll
@@ -472,8 +523,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
             else mfma_v(sn, kop[ks % kAhead], q[ks]);
             if (ks < kPieces) piece(ks);
             if constexpr (F8) {
-              if (ks % 7 == 3) {
-                const int pc = ks / 7;
+              constexpr int kConvIt = (kF8Chunks + kThreads - 1) / kThreads;  // 5 chunks per lane
+              if (ks % 6 == 1 && ks / 6 < kConvIt) {  // read chunk ks / 6
+                const int q2 = tid + kThreads * (ks / 6);
+                conv_x = *reinterpret_cast<const uint4*>(conv_src + (q2 < kF8Chunks ? q2 : 0) * 16);
+              }
+              if (ks % 6 == 4 && ks / 6 < kConvIt) {  // convert and store it
+                const int q2 = tid + kThreads * (ks / 6);
+                const bool real = q2 < kF8Chunks;  // uniform per wave: selects, no branch
+                conv_store(real ? conv_dst : sink, real ? q2 : lane, conv_x);
+              }
+              if (ks >= kKSteps - kDmaN) {  // copies after this wave's conversion reads returned
+                const int pc = ks - (kKSteps - kDmaN);
                 const bool to_sink = wave + 4 * pc >= kF8Pieces;  // uniform: a select, not a branch
                 dma_to(copy_src, to_sink ? (uint32_t)(uintptr_t)sink + wave * 1024 : copy_dst,
                        to_sink ? 0u : copy_stride, pc);
@@ -498,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int par = 0; par < 2; ++par) {
-              vb[h][par] = (i & (kBufs - 1)) * kSubBytes + vbase(h, par);
+              vb[h][par] = buf_of(i) * kSubBytes + vbase(h, par);
               __asm__ volatile("" : "+v"(vb[h][par]));
             }
           constexpr int kSteps = 2 * MB;
