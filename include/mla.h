@@ -250,6 +250,17 @@ int mla_cache_append(const mla_dims* dims, int32_t d_model, const void* h, const
                      float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* mla_cache_append into an FP8 (E4M3) cache (the FP8 latent cache of
+ * mla_decode_fp8): each value of the row [c_t | k^R_t], computed as above in
+ * float32, is divided by kv_scale (float32), saturated to +-448 (a NaN stays
+ * NaN) and rounded to the nearest E4M3 code, ties to the code with an even
+ * mantissa.  kv_cache is [num_blocks,block_size,d_c+d_rope] uint8; kv_scale
+ * finite and > 0.  Workspace and every other argument as for
+ * mla_cache_append. */
+int mla_cache_append_fp8(const mla_dims* dims, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                         float rope_base, float kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                         uint8_t* kv_cache, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- prefill: the non-absorbed forward over whole sequences ------------ */
 
 /* Bytes of device workspace mla_prefill needs for these dims and

@@ -68,6 +68,7 @@ def load() -> ctypes.CDLL:
         "mla_combine_absorb_out_fused": [D, I32],
         "mla_cache_append_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_cache_append": [D, I32, P, P, P, F32, P, P, P, P, SZ, P],
+        "mla_cache_append_fp8": [D, I32, P, P, P, F32, F32, P, P, P, P, SZ, P],
         "mla_prefill_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_prefill": [D, I32, I32, P, P, P, P, P, P, P, F32, I32, P, P, P, SZ, P],
         "mla_version": [],
@@ -304,6 +305,24 @@ def mla_cache_append(dims, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def mla_cache_append_fp8(dims, d_model, h, w_dkv, w_kr, rope_base, kv_scale, block_table, seq_lens, kv_cache,
+                         workspace=None, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    D = d.d_c + d.d_rope
+    if workspace is not None and not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_cache_append_fp8", load().mla_cache_append_fp8(
+        ctypes.byref(d), int(d_model), _ptr(h, "h", st, d.batch * d.q_len * d_model),
+        _ptr(w_dkv, "w_dkv", st, d.d_c * d_model),
+        _ptr(w_kr, "w_kr", st, d.d_rope * d_model) if w_kr is not None else None, float(rope_base),
+        float(kv_scale), _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
+        _ptr(kv_cache, "kv_cache", torch.uint8, d.num_blocks * d.block_size * D), ws_ptr, ws_bytes,
+        _stream(stream)))
 
 
 def mla_prefill_workspace_bytes(dims, total_tokens: int) -> int:

@@ -360,11 +360,14 @@ int mla_cache_append_workspace_bytes(const mla_dims* d, int32_t d_model, size_t*
   return MLA_OK;
 }
 
-int mla_cache_append(const mla_dims* d, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
-                     float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int cache_append_impl(const mla_dims* d, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                      float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
+                      void* workspace, size_t workspace_bytes, void* stream, bool fp8, float kv_scale) {
   int st = check_dims(d);
   if (st != MLA_OK) return st;
+  if (fp8 && !positive_finite(kv_scale)) return MLA_ERR_INVALID_ARG;
   if (d_model < 1 || d_model > kMaxDModel) return MLA_ERR_INVALID_ARG;
   if (!ptr_ok(h) || !ptr_ok(w_dkv) || (d->d_rope > 0 && !ptr_ok(w_kr)) || !ptr_ok(block_table) ||
       !ptr_ok(seq_lens) || !ptr_ok(kv_cache))
@@ -379,10 +382,26 @@ int mla_cache_append(const mla_dims* d, int32_t d_model, const void* h, const vo
     st = device_cus(&cus);
     if (st != MLA_OK) return st;
     return to_status(mla::launch_append_mfma(*d, d_model, cus, h, w_dkv, w_kr, rope_base, block_table, seq_lens,
-                                             kv_cache, static_cast<float*>(workspace), s));
+                                             kv_cache, static_cast<float*>(workspace), s, fp8, kv_scale));
   }
-  return to_status(
-      mla::launch_append_generic(*d, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens, kv_cache, s));
+  return to_status(mla::launch_append_generic(*d, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens,
+                                              kv_cache, s, fp8, kv_scale));
+}
+
+}  // namespace
+
+int mla_cache_append(const mla_dims* d, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                     float rope_base, const int32_t* block_table, const int32_t* seq_lens, void* kv_cache,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return cache_append_impl(d, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens, kv_cache, workspace,
+                           workspace_bytes, stream, false, 1.f);
+}
+
+int mla_cache_append_fp8(const mla_dims* d, int32_t d_model, const void* h, const void* w_dkv, const void* w_kr,
+                         float rope_base, float kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                         uint8_t* kv_cache, void* workspace, size_t workspace_bytes, void* stream) {
+  return cache_append_impl(d, d_model, h, w_dkv, w_kr, rope_base, block_table, seq_lens, kv_cache, workspace,
+                           workspace_bytes, stream, true, kv_scale);
 }
 
 int mla_prefill_workspace_bytes(const mla_dims* d, int32_t total_tokens, size_t* bytes) {

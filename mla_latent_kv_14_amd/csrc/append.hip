@@ -30,6 +30,8 @@
 // float64 so that positions near 2^30 keep their accuracy.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -58,9 +60,29 @@ __device__ __forceinline__ int64_t append_slot(const int32_t* table, const int32
   return ((int64_t)blk * bs + t % bs) * D;
 }
 
+// Store of a column pair into a cache of element type C: the storage type,
+// or (uint8_t) E4M3 codes of x / kv_scale, saturating at +-448 (a NaN stays
+// NaN), rounded to the nearest code with ties to the even one by the
+// hardware conversion.
+template <typename C> struct PairStore {
+  __device__ __forceinline__ static void store(C* dst, float x0, float x1, float) {
+    Storage<C>::store(dst, x0);
+    Storage<C>::store(dst + 1, x1);
+  }
+};
+template <> struct PairStore<uint8_t> {
+  __device__ __forceinline__ static void store(uint8_t* dst, float x0, float x1, float kv_scale) {
+    auto sat = [](float v) { return v != v ? v : fminf(fmaxf(v, -448.f), 448.f); };
+    const float a0 = sat(x0 / kv_scale), a1 = sat(x1 / kv_scale);
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);  // a0 in byte 0, a1 in byte 1
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w & 0xffff);
+  }
+};
+
 // Rotate (x0, x1) if column n lies in the RoPE part, then store the pair.
-template <typename T>
-__device__ __forceinline__ void store_pair(T* dst, int n, int d_c, int d_r, int pos, double base, float x0, float x1) {
+template <typename C>
+__device__ __forceinline__ void store_pair(C* dst, int n, int d_c, int d_r, int pos, double base, float x0, float x1,
+                                           float kv_scale) {
   if (n >= d_c) {
     const int p = (n - d_c) >> 1;
     const double theta = (double)pos / pow(base, 2.0 * p / d_r);
@@ -71,8 +93,7 @@ __device__ __forceinline__ void store_pair(T* dst, int n, int d_c, int d_r, int 
     x0 = (float)y0;
     x1 = (float)y1;
   }
-  Storage<T>::store(dst + n, x0);
-  Storage<T>::store(dst + n + 1, x1);
+  PairStore<C>::store(dst + n, x0, x1, kv_scale);
 }
 
 // ------------------------------------------------------------------ MFMA GEMM
@@ -164,11 +185,12 @@ __global__ __launch_bounds__(kThreads) void append_gemm_mfma(const uint16_t* __r
 // store.  Every partial is requested before the first addition (at most
 // kMaxKSplit of them) and before the token's slot is looked up, so those
 // latencies overlap.
+template <typename C>
 __global__ __launch_bounds__(576) void append_finalize(const float* __restrict__ part, int KS,
                                                        const int32_t* __restrict__ table,
-                                                       const int32_t* __restrict__ seq_lens,
-                                                       uint16_t* __restrict__ cache, int M, int Lq, int bs, int MB,
-                                                       int NB, int d_c, int d_r, double base) {
+                                                       const int32_t* __restrict__ seq_lens, C* __restrict__ cache,
+                                                       int M, int Lq, int bs, int MB, int NB, int d_c, int d_r,
+                                                       double base, float kv_scale) {
   const int m = blockIdx.x, D = d_c + d_r;
   const int p = threadIdx.x;  // one column pair per thread
   float2 v[kMaxKSplit];
@@ -187,18 +209,18 @@ __global__ __launch_bounds__(576) void append_finalize(const float* __restrict__
       x0 += v[k].x;
       x1 += v[k].y;
     }
-  store_pair(cache + off, 2 * p, d_c, d_r, pos, base, x0, x1);
+  store_pair(cache + off, 2 * p, d_c, d_r, pos, base, x0, x1, kv_scale);
 }
 
 // ------------------------------------------------------------------ portable
 // grid (M, ceil(D / 2 / 256)): thread p of token m computes columns 2p, 2p+1.
-template <typename T>
+template <typename T, typename C>
 __global__ __launch_bounds__(kThreads) void append_generic(const T* __restrict__ h, const T* __restrict__ w_dkv,
                                                            const T* __restrict__ w_kr,
                                                            const int32_t* __restrict__ table,
-                                                           const int32_t* __restrict__ seq_lens, T* __restrict__ cache,
+                                                           const int32_t* __restrict__ seq_lens, C* __restrict__ cache,
                                                            int K, int Lq, int bs, int MB, int NB, int d_c, int d_r,
-                                                           double base) {
+                                                           double base, float kv_scale) {
   const int m = blockIdx.x, D = d_c + d_r;
   const int p = blockIdx.y * blockDim.x + threadIdx.x;
   if (p >= D / 2) return;
@@ -226,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void append_generic(const T* __restrict__
   }
   const float x0 = (a0[0] + a0[1]) + (a0[2] + a0[3]);
   const float x1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
-  store_pair(cache + off, n, d_c, d_r, pos, base, x0, x1);
+  store_pair(cache + off, n, d_c, d_r, pos, base, x0, x1, kv_scale);
 }
 
 }  // namespace
@@ -254,7 +276,7 @@ int append_ksplit(const mla_dims& d, int d_model, int cus, int* per_out) {
 
 hipError_t launch_append_mfma(const mla_dims& d, int d_model, int cus, const void* h, const void* w_dkv,
                               const void* w_kr, float rope_base, const int32_t* table, const int32_t* seq_lens,
-                              void* cache, float* part, hipStream_t stream) {
+                              void* cache, float* part, hipStream_t stream, bool fp8, float kv_scale) {
   const int M = d.batch * d.q_len, D = d.d_c + d.d_rope;
   int per = 0;
   const int ks = append_ksplit(d, d_model, cus, &per);
@@ -265,27 +287,36 @@ hipError_t launch_append_mfma(const mla_dims& d, int d_model, int cus, const voi
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int fin_threads = ((D / 2 + 63) / 64) * 64;  // D <= 1088, so at most 576
-  hipLaunchKernelGGL(append_finalize, dim3(M), dim3(fin_threads), 0, stream, part, ks, table, seq_lens,
-                     static_cast<uint16_t*>(cache), M, d.q_len, d.block_size, d.max_blocks_per_seq, d.num_blocks,
-                     d.d_c, d.d_rope, (double)rope_base);
+  if (fp8)
+    hipLaunchKernelGGL(append_finalize<uint8_t>, dim3(M), dim3(fin_threads), 0, stream, part, ks, table, seq_lens,
+                       static_cast<uint8_t*>(cache), M, d.q_len, d.block_size, d.max_blocks_per_seq, d.num_blocks,
+                       d.d_c, d.d_rope, (double)rope_base, kv_scale);
+  else
+    hipLaunchKernelGGL(append_finalize<uint16_t>, dim3(M), dim3(fin_threads), 0, stream, part, ks, table, seq_lens,
+                       static_cast<uint16_t*>(cache), M, d.q_len, d.block_size, d.max_blocks_per_seq, d.num_blocks,
+                       d.d_c, d.d_rope, (double)rope_base, 1.f);
   return hipGetLastError();
 }
 
 hipError_t launch_append_generic(const mla_dims& d, int d_model, const void* h, const void* w_dkv, const void* w_kr,
                                  float rope_base, const int32_t* table, const int32_t* seq_lens, void* cache,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool fp8, float kv_scale) {
   const int M = d.batch * d.q_len, pairs = (d.d_c + d.d_rope) / 2;
   const dim3 grid(M, (pairs + kThreads - 1) / kThreads);
-  if (d.dtype == MLA_BF16)
-    hipLaunchKernelGGL(append_generic<uint16_t>, grid, dim3(kThreads), 0, stream, static_cast<const uint16_t*>(h),
-                       static_cast<const uint16_t*>(w_dkv), static_cast<const uint16_t*>(w_kr), table, seq_lens,
-                       static_cast<uint16_t*>(cache), d_model, d.q_len, d.block_size, d.max_blocks_per_seq,
-                       d.num_blocks, d.d_c, d.d_rope, (double)rope_base);
-  else
-    hipLaunchKernelGGL(append_generic<float>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(h),
-                       static_cast<const float*>(w_dkv), static_cast<const float*>(w_kr), table, seq_lens,
-                       static_cast<float*>(cache), d_model, d.q_len, d.block_size, d.max_blocks_per_seq,
-                       d.num_blocks, d.d_c, d.d_rope, (double)rope_base);
+  auto go = [&](auto hp, auto cp) {
+    using T = std::remove_cv_t<std::remove_pointer_t<decltype(hp)>>;
+    using C = std::remove_pointer_t<decltype(cp)>;
+    hipLaunchKernelGGL((append_generic<T, C>), grid, dim3(kThreads), 0, stream, hp, static_cast<const T*>(w_dkv),
+                       static_cast<const T*>(w_kr), table, seq_lens, cp, d_model, d.q_len, d.block_size,
+                       d.max_blocks_per_seq, d.num_blocks, d.d_c, d.d_rope, (double)rope_base, kv_scale);
+  };
+  if (d.dtype == MLA_BF16) {
+    if (fp8) go(static_cast<const uint16_t*>(h), static_cast<uint8_t*>(cache));
+    else go(static_cast<const uint16_t*>(h), static_cast<uint16_t*>(cache));
+  } else {
+    if (fp8) go(static_cast<const float*>(h), static_cast<uint8_t*>(cache));
+    else go(static_cast<const float*>(h), static_cast<float*>(cache));
+  }
   return hipGetLastError();
 }
 

@@ -50,10 +50,11 @@ int append_max_ksplit();
 int append_ksplit(const mla_dims& d, int d_model, int cus, int* per_out);
 hipError_t launch_append_mfma(const mla_dims& d, int d_model, int cus, const void* h, const void* w_dkv,
                               const void* w_kr, float rope_base, const int32_t* table, const int32_t* seq_lens,
-                              void* cache, float* part, hipStream_t stream);
+                              void* cache, float* part, hipStream_t stream, bool fp8, float kv_scale);
+// fp8: the cache holds E4M3 codes of value / kv_scale
 hipError_t launch_append_generic(const mla_dims& d, int d_model, const void* h, const void* w_dkv, const void* w_kr,
                                  float rope_base, const int32_t* table, const int32_t* seq_lens, void* cache,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool fp8, float kv_scale);
 
 // prefill (prefill.hip): matrix-core path for bf16 with d_c = 512, d_rope = 64,
 // d_nope = d_v = 128; portable path otherwise

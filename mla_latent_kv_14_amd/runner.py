@@ -59,9 +59,15 @@ class DecodeRunner:
         self.append_ws = torch.empty(max(nbytes // 4, 1), dtype=torch.float32, device=dev) if nbytes else None
 
     def cache_append(self, stream=None):
-        """Write the new tokens' rows [W^DKV h | RoPE(W^KR h)] into self.cache."""
-        libmla.mla_cache_append(self.dims, self.app.d_model, self.h, self.w_dkv, self.w_kr, self.app.rope_base,
-                                self.block_table, self.seq_lens, self.cache, self.append_ws, stream)
+        """Write the new tokens' rows [W^DKV h | RoPE(W^KR h)] into self.cache (as E4M3 codes of
+        row / kv_scale for an FP8 cache)."""
+        if self.fp8:
+            libmla.mla_cache_append_fp8(self.dims, self.app.d_model, self.h, self.w_dkv, self.w_kr,
+                                        self.app.rope_base, self.prob.kv_scale, self.block_table, self.seq_lens,
+                                        self.cache, self.append_ws, stream)
+        else:
+            libmla.mla_cache_append(self.dims, self.app.d_model, self.h, self.w_dkv, self.w_kr, self.app.rope_base,
+                                    self.block_table, self.seq_lens, self.cache, self.append_ws, stream)
 
     def absorb_q(self, stream=None):
         libmla.mla_absorb_q(self.dims, self.q_nope, self.q_rope, self.w_uk, self.q_cat, stream)

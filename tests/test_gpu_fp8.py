@@ -213,3 +213,117 @@ def test_fp8_full_batch64_1k8k():
 
 def test_fp8_full_mtp2_lognormal():
     _sampled_check("mtp2_lognormal_fp8", [(0, 0), (17, 15), (64, 7), (127, 3)])
+
+
+# ------------------------------------------------------------------ FP8 append
+
+def _slots(prob):
+    wl = prob.wl
+    out = []
+    for b in range(wl.batch):
+        for j in range(wl.q_len):
+            t = int(prob.seq_lens[b]) - wl.q_len + j
+            out.append((int(prob.block_table[b, t // wl.block_size]), t % wl.block_size, t))
+    return out
+
+
+def _e4m3_half_step(v):
+    """Half the spacing of E4M3 values around |v| (3 mantissa bits; subnormal spacing 2^-9)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6)))
+    return 2.0 ** (e - 4)
+
+
+def _sum_bound(app, rows_h, d_c):
+    """d_model 2^-24 sum_k |h_k| |w_k| per element (float32 sums in any order), RoPE pairs added."""
+    w = np.concatenate([app.f64("w_dkv"), app.f64("w_kr")], axis=0)
+    t = np.abs(rows_h) @ np.abs(w).T
+    pair = t[:, d_c::2] + t[:, d_c + 1::2]
+    t[:, d_c::2] = pair
+    t[:, d_c + 1::2] = pair
+    return app.d_model * 2.0 ** -24 * t
+
+
+def _append_fp8_check(prob):
+    from mla_latent_kv_14_amd.inputs import make_append_inputs
+    wl = prob.wl
+    app = make_append_inputs(prob)
+    say(f"case FP8 append {wl.name} B={wl.batch} Lq={wl.q_len} d_model={app.d_model} "
+        f"lens={prob.seq_lens.tolist()[:8]}")
+    r = DecodeRunner(prob)
+    r.setup_append(app)
+    before = r.cache.clone()
+    r.cache_append()
+    torch.cuda.synchronize()
+    after = r.cache
+    slots = _slots(prob)
+    blk = torch.tensor([s[0] for s in slots], device=after.device)
+    slot = torch.tensor([s[1] for s in slots], device=after.device)
+    got = after[blk, slot].cpu().numpy()
+    h = app.f64("h").reshape(wl.batch * wl.q_len, app.d_model)
+    pos = np.array([s[2] for s in slots], dtype=np.int64)
+    v64 = orc.cache_rows_reference(h, app.f64("w_dkv"), app.f64("w_kr"), pos, app.rope_base) / prob.kv_scale
+    assert np.abs(v64).max() < orc.E4M3_MAX  # no saturation in these inputs
+    ref32 = orc.cache_append_fp8_reference(prob.cache.numpy(), prob.block_table, prob.seq_lens, app.f64("h"),
+                                           app.f64("w_dkv"), app.f64("w_kr"), prob.kv_scale, app.rope_base,
+                                           row_dtype=np.float32)
+    ref_codes = ref32[[s[0] for s in slots], [s[1] for s in slots]]
+    exact = float((got == ref_codes).mean())
+    lim = _e4m3_half_step(v64) + _sum_bound(app, h, wl.d_c) / prob.kv_scale
+    worst = float(np.max(np.abs(orc.e4m3_decode(got) - v64) / lim))
+    say(f"  codes equal to the oracle's float32 decision: {100 * exact:.3f}%; worst error / bound = {worst:.3f}")
+    assert exact >= 0.95
+    assert worst <= 1.0
+    mask = torch.ones(before.shape[:2], dtype=torch.bool, device=before.device)
+    mask[blk, slot] = False
+    assert torch.equal(after[mask], before[mask]), "the FP8 append wrote outside the new tokens' slots"
+    return r, app
+
+
+def test_fp8_append_tiny_f32():
+    _append_fp8_check(make_problem(workload("tiny_f32_fp8"), 1000))
+
+
+def test_fp8_append_bf16_ragged():
+    wl = workload("single_4k_fp8", batch=6, lengths=("fixed", (1, 31, 33, 64, 65, 1000)))
+    _append_fp8_check(make_problem(wl, 2110))
+
+
+def test_fp8_append_mtp2_block_edges():
+    wl = workload("mtp2_lognormal_fp8", batch=5, lengths=("fixed", (2, 64, 65, 129, 700)))
+    _append_fp8_check(make_problem(wl, 2111))
+
+
+def test_fp8_append_full_batch64():
+    _append_fp8_check(make_problem(workload("batch64_1k8k_fp8")))
+
+
+def test_fp8_append_portable_and_mfma_agree(monkeypatch):
+    wl = workload("single_4k_fp8", batch=3, lengths=("fixed", (5, 70, 700)))
+    p = make_problem(wl, 2112)
+    r1, _ = _append_fp8_check(p)
+    monkeypatch.setenv("MLA_KERNELS", "portable")
+    r2, _ = _append_fp8_check(p)
+    monkeypatch.delenv("MLA_KERNELS")
+    same = float((r1.cache == r2.cache).float().mean())
+    say(f"  matrix-core vs portable append: {100 * same:.4f}% of codes equal")
+    assert same >= 0.999
+
+
+def test_fp8_append_then_decode():
+    """The FP8 decode reads the codes the FP8 append wrote: the GPU's append + decode against the oracle's
+    append (its own codes, float32 decisions) + decode over the decoded cache."""
+    from mla_latent_kv_14_amd.inputs import make_append_inputs
+    wl = workload("single_4k_fp8", batch=4, lengths=("fixed", (1, 70, 640, 3000)))
+    p = make_problem(wl, 2113)
+    app = make_append_inputs(p)
+    r = DecodeRunner(p)
+    r.setup_append(app)
+    r.cache_append()
+    r.step()
+    torch.cuda.synchronize()
+    codes = orc.cache_append_fp8_reference(p.cache.numpy(), p.block_table, p.seq_lens, app.f64("h"),
+                                           app.f64("w_dkv"), app.f64("w_kr"), p.kv_scale, app.rope_base,
+                                           row_dtype=np.float32)
+    u, _, _ = orc.mla_decode_reference(p.f64("q_nope"), p.f64("q_rope"), orc.fp8_cache_values(codes, p.kv_scale),
+                                       p.block_table, p.seq_lens, p.f64("w_uk"), p.f64("w_uv"), p.scale, wl.d_c)
+    assert_parity(to64(r.u), u, wl.dtype, "u after FP8 append")
