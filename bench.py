@@ -42,23 +42,29 @@ def log(msg):
 def algorithmic_work(prob):
     """Bytes and flops the attention kernel must move / do for one launch.
 
-    Bytes: every visible cache row once (d_c + d_rope elements), the absorbed
-    queries, the block-table entries used, the sequence lengths, and the
-    latent output o (float32).  Split partials are implementation overhead
-    and not counted.  Flops: 2 * (d_c + d_rope) for the score plus 2 * d_c
-    for the weighted sum, per visible (query row, token) pair.
+    Bytes: every visible cache row once (d_c + d_rope elements, one byte each
+    for an FP8 cache), the absorbed queries, the block-table entries used, the
+    sequence lengths, and the latent output o (float32).  Split partials are
+    implementation overhead and not counted.  Flops: 2 * (d_c + d_rope) for
+    the score plus 2 * d_c for the weighted sum, per visible (query row,
+    token) pair.
     """
     wl = prob.wl
     esz = 4 if wl.dtype == "f32" else 2
     D = wl.d_c + wl.d_rope
     L = prob.seq_lens.astype(np.int64)
-    rows_bytes = int(L.sum()) * D * esz
+    rows_bytes = int(L.sum()) * D * (1 if prob.fp8 else esz)
     q_bytes = wl.batch * wl.q_len * wl.heads * D * esz
     table_bytes = int(((L + wl.block_size - 1) // wl.block_size).sum()) * 4 + wl.batch * 4
     o_bytes = wl.batch * wl.q_len * wl.heads * wl.d_c * 4
     visible = sum(int((L - wl.q_len + j + 1).sum()) for j in range(wl.q_len))
     flops = 2 * wl.heads * visible * (D + wl.d_c)
     return rows_bytes + q_bytes + table_bytes + o_bytes, flops
+
+
+def tokens_of(prob):
+    """New tokens one decode step produces: B * q_len."""
+    return prob.wl.batch * prob.wl.q_len
 
 
 def append_work(prob, d_model):
@@ -150,6 +156,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays instead of eager launches")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache twin of the workload")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -159,7 +166,7 @@ def main():
 
     import torch
 
-    from mla_latent_kv_14_amd.inputs import make_append_inputs, make_prefill_problem, make_problem, workload
+    from mla_latent_kv_14_amd.inputs import WORKLOADS, make_append_inputs, make_prefill_problem, make_problem, workload
     from mla_latent_kv_14_amd.runner import DecodeRunner, PrefillRunner
 
     if not torch.cuda.is_available():
@@ -275,6 +282,42 @@ def main():
         log(f"bench: prefill {PREFILL_WORKLOAD}: {pms:.2f} ms, {prefill['tflops']:.0f} TFLOP/s")
         del pr
 
+    # the same step over an FP8 (E4M3) cache: the workload's FP8 twin (same
+    # draws, codes of value / kv_scale)
+    fp8 = None
+    twin = wl.name.replace("_bf16", "_fp8")
+    if not args.no_fp8 and not prob.fp8 and twin in WORKLOADS:
+        fprob = make_problem(workload(twin), args.seed)
+        fr = DecodeRunner(fprob, device="cuda:0")
+        fcalls = [fr.plan, fr.absorb_q, fr.decode_planned, fr.combine_absorb_out]
+        for _ in range(args.warmup):
+            for fn in fcalls:
+                fn()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for i in range(K):
+            for fn in fcalls:
+                fn()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        f_step = f0.elapsed_time(f1) / K
+        torch.cuda.synchronize()
+        f0.record(stream)
+        for i in range(K):
+            fr.decode_planned()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        f_kernel_us = 1e3 * f0.elapsed_time(f1) / K
+        f_bytes, _ = algorithmic_work(fprob)
+        fp8 = {"workload": twin, "kv_scale": fprob.kv_scale, "ms_per_step": f_step,
+               "tokens_per_s": tokens_of(fprob) / (f_step * 1e-3), "attention_kernel_us": f_kernel_us,
+               "alg_bytes_per_launch": f_bytes, "gbs": f_bytes / (f_kernel_us * 1e-6) / 1e9,
+               "hbm_frac": f_bytes / (f_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+               "cache_bytes": int(fprob.cache.numel()), "num_splits": fr.num_splits}
+        log(f"bench: FP8 cache ({twin}): {f_step * 1e3:.1f} us/step, attention {f_kernel_us:.1f} us")
+        del fr
+
     alg_bytes, flops = algorithmic_work(prob)
     dec_s = decode_kernel_us * 1e-6
     achieved_gbs = alg_bytes / dec_s / 1e9
@@ -315,6 +358,7 @@ def main():
         "step_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "fp8_cache": fp8,
         "cache_append": {"us_per_call": append_us, "d_model": app.d_model, "alg_bytes": ap_bytes,
                          "gbs": ap_bytes / (append_us * 1e-6) / 1e9,
                          "hbm_frac": ap_bytes / (append_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
