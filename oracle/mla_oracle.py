@@ -56,6 +56,10 @@ __all__ = [
     "e4m3_encode",
     "fp8_cache_values",
     "cache_append_fp8_reference",
+    "fold_query_weight_reference",
+    "fused_query_reference",
+    "fold_output_weight_reference",
+    "fused_output_reference",
 ]
 
 
@@ -430,3 +434,60 @@ def cache_append_fp8_reference(codes, block_table, seq_lens, h, w_dkv, w_kr, kv_
             row = cache_rows_reference(h[b, j], w_dkv, w_kr, pos, base).astype(row_dtype)
             out[int(block_table[b, pos // bs]), pos % bs, :] = e4m3_encode(row / row_dtype(kv_scale))
     return out
+
+
+# --------------------------------------------------------------------------
+# Offline weight folds.  "DeepSeek-V3 MLA: Multi-Head Latent Attention
+# Guide", Matrix Absorption Trick section 3: the final output W^O [u_1; ...;
+# u_nh] equals W~^O [o_1; ...; o_nh], W~^O being W^O multiplied offline by the
+# heads' up-projections W^UV_i; "Deconstructing DeepSeek V4 Pro", Practical
+# Deployment: the query projection and W^UK^T can likewise be multiplied into
+# one fused query weight before serving.  Readings: the query projection is
+# given per head as W_in[h] in R^{d_nope x d_in} (the content part of the
+# query up-projection W^UQ of the query latent c^Q, d_in = d_c' = 1536 in the
+# Guide's module and the V2 note's table, or a projection of the hidden state
+# itself), so the fused weight is W~_Q[h] = W^UK_h^T W_in[h] in
+# R^{d_c x d_in}; W^O in R^{d_out x (n_h d_v)} acts on the heads' outputs
+# concatenated in head order, so W~^O = W^O blockdiag(W^UV_1, ..., W^UV_nh) in
+# R^{d_out x (n_h d_c)}.
+
+
+def fold_query_weight_reference(w_in, w_uk):
+    """W~_Q[h] = (W^UK_h)^T W_in[h]: w_in [H, d_nope, d_in], w_uk [H, d_nope, d_c] -> [H, d_c, d_in]."""
+    w_in = np.asarray(w_in, dtype=np.float64)
+    w_uk = np.asarray(w_uk, dtype=np.float64)
+    return np.stack([w_uk[h].T @ w_in[h] for h in range(w_in.shape[0])])
+
+
+def fused_query_reference(x, q_rope, w_fused):
+    """q_cat[b,j,h] = [W~_Q[h] x[b,j] ; q^R_{b,j,h}]: x [B, Lq, d_in], q_rope [B, Lq, H, d_rope],
+    w_fused [H, d_c, d_in] -> [B, Lq, H, d_c + d_rope] (what mla_absorb_q gives from q^C = W_in x)."""
+    x = np.asarray(x, dtype=np.float64)
+    q_rope = np.asarray(q_rope, dtype=np.float64)
+    w_fused = np.asarray(w_fused, dtype=np.float64)
+    B, Lq, _ = x.shape
+    H, d_c, _ = w_fused.shape
+    out = np.zeros((B, Lq, H, d_c + q_rope.shape[3]))
+    out[:, :, :, d_c:] = q_rope  # the RoPE part passes through
+    for h in range(H):
+        out[:, :, h, :d_c] = x @ w_fused[h].T
+    return out
+
+
+def fold_output_weight_reference(w_o, w_uv, rows=None):
+    """W~^O = W^O blockdiag(W^UV_h): w_o [d_out, H d_v], w_uv [H, d_v, d_c] -> [d_out, H d_c];
+    column block h is W^O[:, h d_v:(h+1) d_v] W^UV_h.  ``rows`` restricts the result to those rows."""
+    w_o = np.asarray(w_o, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    if rows is not None:
+        w_o = w_o[np.asarray(rows)]
+    H, d_v, d_c = w_uv.shape
+    return np.concatenate([w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[h] for h in range(H)], axis=1)
+
+
+def fused_output_reference(o, w_fused):
+    """y[b,j] = W~^O [o_{b,j,1}; ...; o_{b,j,H}]: o [B, Lq, H, d_c], w_fused [d_out, H d_c] -> [B, Lq, d_out]."""
+    o = np.asarray(o, dtype=np.float64)
+    w_fused = np.asarray(w_fused, dtype=np.float64)
+    B, Lq, H, d_c = o.shape
+    return o.reshape(B, Lq, H * d_c) @ w_fused.T

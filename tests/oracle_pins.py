@@ -27,7 +27,11 @@ Independent routes used here:
     implementation of the same format), values the format's definition fixes
     (1, 2, 1.5, 448, the smallest normal and subnormal, -0), a pure-Python
     nearest-code search over all finite codes, and the float cache append
-    rounded through torch.
+    rounded through torch;
+  * for the weight folds: the unfolded route of the same pages (W_in x, then
+    the absorbed query; W^UV after the latent sum, then W^O) through the
+    pinned absorb_q / absorb_out references and plain matrix products, and
+    scalar loops on tiny sizes.
 """
 from __future__ import annotations
 
@@ -608,6 +612,64 @@ def pin_cache_append_fp8(orc, seed=35):
     assert np.array_equal(got[~written], codes[~written])
 
 
+# ------------------------------------------------------------------ offline weight folds
+
+class TinyFold:
+    def __init__(self, seed, H=3, d_n=4, d_v=5, d_c=6, d_r=2, d_in=7, d_out=8, B=2, Lq=2):
+        rng = np.random.default_rng(seed)
+        self.w_in = rng.standard_normal((H, d_n, d_in))
+        self.w_uk = rng.standard_normal((H, d_n, d_c))
+        self.w_uv = rng.standard_normal((H, d_v, d_c))
+        self.w_o = rng.standard_normal((d_out, H * d_v))
+        self.x = rng.standard_normal((B, Lq, d_in))
+        self.q_rope = rng.standard_normal((B, Lq, H, d_r))
+        self.o = rng.standard_normal((B, Lq, H, d_c))
+
+
+def pin_fused_query_equals_unfolded(orc, seed=40):
+    """Fused query weight on x equals the unfolded route: q^C = W_in x per head, then absorb_q."""
+    p = TinyFold(seed)
+    q_nope = np.einsum("hnd,bjd->bjhn", p.w_in, p.x)
+    ref = orc.absorb_q_reference(q_nope, p.q_rope, p.w_uk)
+    got = orc.fused_query_reference(p.x, p.q_rope, orc.fold_query_weight_reference(p.w_in, p.w_uk))
+    _close(got, ref)
+
+
+def pin_fused_output_equals_unfolded(orc, seed=41):
+    """Fused output weight on the latent sums equals W^O applied to the heads' u = W^UV o, concatenated."""
+    p = TinyFold(seed)
+    u = orc.absorb_out_reference(p.o, p.w_uv)  # [B, Lq, H, d_v]
+    ref = u.reshape(u.shape[0], u.shape[1], -1) @ p.w_o.T
+    got = orc.fused_output_reference(p.o, orc.fold_output_weight_reference(p.w_o, p.w_uv))
+    _close(got, ref)
+
+
+def pin_folds_bruteforce(orc, seed=42):
+    """Both folds against scalar loops, and the row-restricted output fold against the whole."""
+    p = TinyFold(seed)
+    H, d_n, d_in = p.w_in.shape
+    d_c = p.w_uk.shape[2]
+    fq = orc.fold_query_weight_reference(p.w_in, p.w_uk)
+    for h in range(H):
+        for c in range(d_c):
+            for i in range(d_in):
+                _close(fq[h, c, i], sum(p.w_uk[h, n, c] * p.w_in[h, n, i] for n in range(d_n)))
+    fo = orc.fold_output_weight_reference(p.w_o, p.w_uv)
+    d_out = p.w_o.shape[0]
+    d_v = p.w_uv.shape[1]
+    for r in range(d_out):
+        for h in range(H):
+            for c in range(d_c):
+                want = sum(p.w_o[r, h * d_v + v] * p.w_uv[h, v, c] for v in range(d_v))
+                _close(fo[r, h * d_c + c], want)
+    _close(orc.fold_output_weight_reference(p.w_o, p.w_uv, rows=[5, 1]), fo[[5, 1]])
+    y = orc.fused_output_reference(p.o, fo)
+    for b in range(p.o.shape[0]):
+        for j in range(p.o.shape[1]):
+            for r in range(d_out):
+                _close(y[b, j, r], sum(fo[r, h * d_c + c] * p.o[b, j, h, c] for h in range(H) for c in range(d_c)))
+
+
 ALL_PINS = [
     pin_absorbed_route,
     pin_library_sdpa,
@@ -637,4 +699,7 @@ ALL_PINS = [
     pin_e4m3_encode_library,
     pin_fp8_cache_values,
     pin_cache_append_fp8,
+    pin_fused_query_equals_unfolded,
+    pin_fused_output_equals_unfolded,
+    pin_folds_bruteforce,
 ]

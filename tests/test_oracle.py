@@ -118,6 +118,13 @@ MUTATIONS = {
     "append_fp8_wrong_slot": ("out[int(block_table[b, pos // bs]), pos % bs, :] = e4m3_encode(",
                               "out[int(block_table[b, pos // bs]), (pos + 1) % bs, :] = e4m3_encode("),
     "append_fp8_position_off_by_one": ("pos = int(seq_lens[b]) - Lq + j  #", "pos = int(seq_lens[b]) - Lq + j - 1  #"),
+    "fold_query_rows_reversed": ("np.stack([w_uk[h].T @ w_in[h] for h in range(w_in.shape[0])])",
+                                 "np.stack([(w_uk[h].T @ w_in[h])[::-1] for h in range(w_in.shape[0])])"),
+    "fused_query_rope_dropped": ("out[:, :, :, d_c:] = q_rope  #", "out[:, :, :, d_c:] = 0.0 * q_rope  #"),
+    "fold_output_wrong_block": ("w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[h] for h in range(H)",
+                                "w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[(h + 1) % H] for h in range(H)"),
+    "fused_output_columns_reversed": ("return o.reshape(B, Lq, H * d_c) @ w_fused.T",
+                                      "return o.reshape(B, Lq, H * d_c) @ w_fused[:, ::-1].T"),
 }
 
 
