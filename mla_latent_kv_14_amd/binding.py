@@ -71,6 +71,11 @@ def load() -> ctypes.CDLL:
         "mla_cache_append_fp8": [D, I32, P, P, P, F32, F32, P, P, P, P, SZ, P],
         "mla_prefill_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_prefill": [D, I32, I32, P, P, P, P, P, P, P, F32, I32, P, P, P, SZ, P],
+        "mla_fold_query_weight": [D, I32, P, P, P, P],
+        "mla_fused_query": [D, I32, P, P, P, P, P],
+        "mla_fold_output_weight": [D, I32, P, P, P, P],
+        "mla_fused_output_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
+        "mla_fused_output": [D, I32, P, P, P, P, SZ, P],
         "mla_version": [],
     }
     for name, args in sig.items():
@@ -322,6 +327,54 @@ def mla_cache_append_fp8(dims, d_model, h, w_dkv, w_kr, rope_base, kv_scale, blo
         float(kv_scale), _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch),
         _ptr(kv_cache, "kv_cache", torch.uint8, d.num_blocks * d.block_size * D), ws_ptr, ws_bytes,
+        _stream(stream)))
+
+
+def mla_fold_query_weight(dims, d_in, w_in, w_uk, w_fused, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    H = d.num_heads
+    _check("mla_fold_query_weight", load().mla_fold_query_weight(
+        ctypes.byref(d), int(d_in), _ptr(w_in, "w_in", st, H * d.d_nope * d_in),
+        _ptr(w_uk, "w_uk", st, H * d.d_nope * d.d_c), _ptr(w_fused, "w_fused", st, H * d.d_c * d_in),
+        _stream(stream)))
+
+
+def mla_fused_query(dims, d_in, x, q_rope, w_fused, q_cat, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    M, H = d.batch * d.q_len, d.num_heads
+    _check("mla_fused_query", load().mla_fused_query(
+        ctypes.byref(d), int(d_in), _ptr(x, "x", st, M * d_in),
+        _ptr(q_rope, "q_rope", st, M * H * d.d_rope) if d.d_rope > 0 else None,
+        _ptr(w_fused, "w_fused", st, H * d.d_c * d_in), _ptr(q_cat, "q_cat", st, M * H * (d.d_c + d.d_rope)),
+        _stream(stream)))
+
+
+def mla_fold_output_weight(dims, d_out, w_o, w_uv, w_fused, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    H = d.num_heads
+    _check("mla_fold_output_weight", load().mla_fold_output_weight(
+        ctypes.byref(d), int(d_out), _ptr(w_o, "w_o", st, d_out * H * d.d_v),
+        _ptr(w_uv, "w_uv", st, H * d.d_v * d.d_c), _ptr(w_fused, "w_fused", st, d_out * H * d.d_c),
+        _stream(stream)))
+
+
+def mla_fused_output_workspace_bytes(dims, d_out: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_fused_output_workspace_bytes",
+           load().mla_fused_output_workspace_bytes(ctypes.byref(dims), int(d_out), ctypes.byref(out)))
+    return out.value
+
+
+def mla_fused_output(dims, d_out, o_latent, w_fused, y, workspace=None, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    M, H = d.batch * d.q_len, d.num_heads
+    if workspace is not None and not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_fused_output", load().mla_fused_output(
+        ctypes.byref(d), int(d_out), _ptr(o_latent, "o_latent", torch.float32, M * H * d.d_c),
+        _ptr(w_fused, "w_fused", st, d_out * H * d.d_c), _ptr(y, "y", st, M * d_out), ws_ptr, ws_bytes,
         _stream(stream)))
 
 

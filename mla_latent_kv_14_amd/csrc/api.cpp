@@ -434,6 +434,64 @@ int mla_prefill(const mla_dims* d, int32_t total_tokens, int32_t max_seqlen, con
                                        w_uv, softmax_scale, causal, out, lse, workspace, mfma, (hipStream_t)stream));
 }
 
+int mla_fold_query_weight(const mla_dims* d, int32_t d_in, const void* w_in, const void* w_uk, void* w_fused,
+                          void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d_in < 1 || d_in > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(w_in) || !ptr_ok(w_uk) || !ptr_ok(w_fused)) return MLA_ERR_INVALID_ARG;
+  return to_status(mla::launch_fold_query(*d, d_in, w_in, w_uk, w_fused, (hipStream_t)stream));
+}
+
+int mla_fused_query(const mla_dims* d, int32_t d_in, const void* x, const void* q_rope, const void* w_fused,
+                    void* q_cat, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d_in < 1 || d_in > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(x) || !ptr_ok(w_fused) || !ptr_ok(q_cat) || (d->d_rope > 0 && !ptr_ok(q_rope)))
+    return MLA_ERR_INVALID_ARG;
+  const bool mfma = !force_generic() && mla::fused_query_mfma_supported(*d, d_in);
+  int cus = 1;
+  if (mfma && (st = device_cus(&cus)) != MLA_OK) return st;
+  return to_status(mla::launch_fused_query(*d, d_in, cus, x, q_rope, w_fused, q_cat, mfma, (hipStream_t)stream));
+}
+
+int mla_fold_output_weight(const mla_dims* d, int32_t d_out, const void* w_o, const void* w_uv, void* w_fused,
+                           void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d_out < 1 || d_out > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(w_o) || !ptr_ok(w_uv) || !ptr_ok(w_fused)) return MLA_ERR_INVALID_ARG;
+  return to_status(mla::launch_fold_output(*d, d_out, w_o, w_uv, w_fused, (hipStream_t)stream));
+}
+
+int mla_fused_output_workspace_bytes(const mla_dims* d, int32_t d_out, size_t* bytes) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr || d_out < 1 || d_out > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  size_t b = 0;
+  if (mla::fused_output_mfma_supported(*d, d_out))  // float32 split-K partials [KS, B*Lq, d_out]
+    b = (size_t)mla::linear_max_ksplit() * d->batch * d->q_len * d_out * sizeof(float);
+  *bytes = (b + 255) / 256 * 256;
+  return MLA_OK;
+}
+
+int mla_fused_output(const mla_dims* d, int32_t d_out, const float* o_latent, const void* w_fused, void* y,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d_out < 1 || d_out > kMaxDModel) return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(o_latent) || !ptr_ok(w_fused) || !ptr_ok(y)) return MLA_ERR_INVALID_ARG;
+  size_t need = 0;
+  mla_fused_output_workspace_bytes(d, d_out, &need);
+  if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need)) return MLA_ERR_INVALID_ARG;
+  const bool mfma = !force_generic() && mla::fused_output_mfma_supported(*d, d_out);
+  int cus = 1;
+  if (mfma && (st = device_cus(&cus)) != MLA_OK) return st;
+  return to_status(mla::launch_fused_output(*d, d_out, cus, o_latent, w_fused, y, static_cast<float*>(workspace),
+                                            mfma, (hipStream_t)stream));
+}
+
 int mla_combine_absorb_out_fused(const mla_dims* d, int32_t num_splits) {
   if (check_dims(d) != MLA_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
   return (!force_generic() && mla::absorb_mfma_supported(*d) && num_splits <= mla::combine_out_max_splits()) ? 1 : 0;

@@ -41,6 +41,17 @@ from ``PCG64([seed, 0x9F11])``: lengths by the workload's distribution, then
 the tokens' latents c ~ N(0, 1), RoPE keys ~ N(0, 1), q_nope, q_rope ~ N(0, 1)
 per (token, head), then W_UK, W_UV ~ N(0, 1)/sqrt(d_c); the tokens of all
 sequences are packed in sequence order.
+
+Weight-fold inputs (``make_fold_inputs``) come from ``PCG64([seed, 0xF01D])``:
+the query projection's input x ~ N(0, 1) of width d_in (1536, the query
+latent width of the DeepSeek-V2/V3 shapes), the per-head content query
+projection W_in ~ N(0, 1)/sqrt(d_in) [H, d_nope, d_in], the output projection
+W^O ~ N(0, 1)/sqrt(H d_v) [d_out, H d_v] (d_out = the model width, 7168), and
+a merged latent attention output o ~ N(0, 1)/4 in float32 [B, Lq, H, d_c] (a
+softmax-weighted mean of unit-variance latent rows, so well under 1).
+``synthetic_fused_output_weight`` draws a stand-in for W~^O ~ N(0, 1)/256
+[d_out, H d_c] from ``PCG64([seed, 0xF01E])`` for the full-size product test,
+where folding the real weight in float64 would take minutes.
 """
 from __future__ import annotations
 
@@ -52,7 +63,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "Problem", "make_problem", "workload", "AppendInputs", "make_append_inputs",
-           "PrefillProblem", "make_prefill_problem"]
+           "PrefillProblem", "make_prefill_problem", "FoldInputs", "make_fold_inputs", "synthetic_fused_output_weight"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -327,3 +338,45 @@ def make_prefill_problem(wl: Workload, seed: Optional[int] = None, seq_lens: Opt
     w_uk = _store(rng.standard_normal((wl.heads, wl.d_nope, wl.d_c)) * inv, wl.dtype)
     w_uv = _store(rng.standard_normal((wl.heads, wl.d_v, wl.d_c)) * inv, wl.dtype)
     return PrefillProblem(wl, seed, lens, cu, q_nope, q_rope, c_kv, k_rope, w_uk, w_uv)
+
+
+@dataclasses.dataclass
+class FoldInputs:
+    """Inputs of the weight folds and the fused products.  CPU tensors, storage dtype (o: float32)."""
+
+    d_in: int
+    d_out: int
+    x: torch.Tensor  # [B, Lq, d_in]
+    w_in: torch.Tensor  # [H, d_nope, d_in]
+    w_o: torch.Tensor  # [d_out, H * d_v]
+    o: torch.Tensor  # [B, Lq, H, d_c] float32
+
+    def f64(self, name: str) -> np.ndarray:
+        return getattr(self, name).to(torch.float64).numpy()
+
+
+def make_fold_inputs(prob: Problem, d_in: int = 1536, d_out: Optional[int] = None) -> FoldInputs:
+    """Draw the fold inputs belonging to ``prob`` (its q_rope, W_UK and W_UV complete them)."""
+    wl = prob.wl
+    d_out = wl.d_model if d_out is None else int(d_out)
+    rng = np.random.Generator(np.random.PCG64([prob.seed, 0xF01D]))
+    x = _store(rng.standard_normal((wl.batch, wl.q_len, d_in)), wl.dtype)
+    w_in = _store(rng.standard_normal((wl.heads, wl.d_nope, d_in)) / math.sqrt(d_in), wl.dtype)
+    w_o = _store(rng.standard_normal((d_out, wl.heads * wl.d_v)) / math.sqrt(wl.heads * wl.d_v), wl.dtype)
+    o = torch.from_numpy((rng.standard_normal((wl.batch, wl.q_len, wl.heads, wl.d_c)) / 4).astype(np.float32))
+    return FoldInputs(d_in, d_out, x, w_in, w_o, o)
+
+
+def synthetic_fused_output_weight(prob: Problem, d_out: int) -> torch.Tensor:
+    """A stand-in fused output weight [d_out, H d_c] in the storage dtype, drawn in float32 row blocks."""
+    wl = prob.wl
+    rng = np.random.Generator(np.random.PCG64([prob.seed, 0xF01E]))
+    K = wl.heads * wl.d_c
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    out = torch.empty((d_out, K), dtype=dt)
+    step = 256
+    for r in range(0, d_out, step):
+        n = min(step, d_out - r)
+        blk = rng.standard_normal((n, K), dtype=np.float32) / np.float32(256.0)
+        out[r:r + n] = torch.from_numpy(blk).to(dt)
+    return out

@@ -230,3 +230,48 @@ def test_prefill_bf16_workspace_limit():
     need = libmla.mla_prefill_workspace_bytes(bf, T)
     assert need >= 1 << 32
     assert _prefill(bf, T=T, maxlen=T, ws_bytes=need) == libmla.MLA_ERR_UNSUPPORTED
+
+
+def test_fused_output_workspace_bytes():
+    bf = _dims(dtype=libmla.MLA_BF16, batch=64, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128,
+               block_size=64)
+    n = libmla.mla_fused_output_workspace_bytes(bf, 7168)
+    assert n % 256 == 0 and n >= 64 * 7168 * 4  # float32 partials, at least one split
+    assert libmla.mla_fused_output_workspace_bytes(bf, 7168 + 32) == 0  # not a multiple of 64: portable kernel
+    assert libmla.mla_fused_output_workspace_bytes(_dims(), 64) == 0  # float32 storage: portable kernel
+    out = ctypes.c_size_t(0)
+    for dout in (0, -1, 1 << 17):
+        assert _call("mla_fused_output_workspace_bytes", ctypes.byref(bf), dout, ctypes.byref(out)) == -1
+    assert _call("mla_fused_output_workspace_bytes", ctypes.byref(bf), 7168, None) == -1
+
+
+@pytest.mark.parametrize("over", [
+    {"a": None}, {"b": None}, {"c": None}, {"a": P(FAKE + 2)}, {"c": P(FAKE + 8)}, {"n": 0}, {"n": 1 << 17},
+])
+@pytest.mark.parametrize("fn", ["mla_fold_query_weight", "mla_fold_output_weight"])
+def test_fold_invalid_args(fn, over):
+    args = dict(n=96, a=P(FAKE), b=P(FAKE), c=P(FAKE))
+    args.update(over)
+    assert _call(fn, ctypes.byref(_dims()), args["n"], args["a"], args["b"], args["c"], None) == -1
+
+
+@pytest.mark.parametrize("over", [
+    {"x": None}, {"w": None}, {"q": None}, {"r": None}, {"x": P(FAKE + 4)}, {"d_in": 0}, {"d_in": 1 << 17},
+])
+def test_fused_query_invalid_args(over):
+    args = dict(d_in=96, x=P(FAKE), r=P(FAKE), w=P(FAKE), q=P(FAKE))
+    args.update(over)
+    assert _call("mla_fused_query", ctypes.byref(_dims()), args["d_in"], args["x"], args["r"], args["w"],
+                 args["q"], None) == -1
+
+
+@pytest.mark.parametrize("over", [
+    {"o": None}, {"w": None}, {"y": None}, {"o": P(FAKE + 4)}, {"d_out": 0}, {"d_out": 1 << 17},
+    {"ws": None}, {"ws_bytes": 0}, {"ws": P(FAKE + 4)},
+])
+def test_fused_output_invalid_args(over):
+    bf = _dims(dtype=libmla.MLA_BF16, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128, block_size=64)
+    args = dict(d_out=256, o=P(FAKE), w=P(FAKE), y=P(FAKE), ws=P(FAKE), ws_bytes=1 << 24)
+    args.update(over)
+    assert _call("mla_fused_output", ctypes.byref(bf), args["d_out"], args["o"], args["w"], args["y"], args["ws"],
+                 args["ws_bytes"], None) == -1

@@ -1,0 +1,340 @@
+"""GPU parity of the offline weight folds and the fused products against the float64 oracle.
+
+mla_fold_query_weight, mla_fold_output_weight, mla_fused_query and
+mla_fused_output, called through the C-ABI.  Every input of a product test is
+the oracle's (the folded weight is the oracle's fold, rounded once to the
+storage type); the end-to-end tests compare the library's fold followed by its
+product with the unfolded route of the oracle.
+
+Bars (written per test): float32 max-abs 1e-5; bf16 max-abs 2e-2 and relative
+L2 1e-2.  On top, each element must lie within the bound the arithmetic
+gives: half a step of the output type around the oracle, plus the float32
+summation bound K 2^-24 sum_k |a_k| |b_k| (any order of the K additions),
+plus, for the matrix-core output product, 2^-17 sum_k |a_k| |b_k| for the
+bf16 hi + lo split of the float32 input.  For the bf16 folds at least 95% of
+the elements must equal the oracle rounded to bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_14_amd import binding as libmla
+from mla_latent_kv_14_amd.inputs import make_fold_inputs, make_problem, synthetic_fused_output_weight, workload
+from oracle import mla_oracle as orc
+from tests.gpu_common import assert_parity, require_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+
+
+# small shapes: several MFMA tiles and split-K chunks, rows that fill no tile
+SMALL = dict(heads=8, d_c=128, d_rope=64, d_nope=32, d_v=48, lengths=("fixed", (64, 64, 64)), batch=3, q_len=2)
+SMALL_IO = (192, 320)  # d_in, d_out: both on the matrix cores for bf16
+RAGGED_IO = (100, 100)  # neither a multiple of 64: portable kernels
+
+
+def _problem(name, **over):
+    wl = workload(name, **over)
+    prob = make_problem(wl, seq_lens=np.full(wl.batch, max(wl.q_len, 16), dtype=np.int32))
+    return wl, prob
+
+
+def _dims(wl, prob):
+    return libmla.make_dims(wl.batch, wl.q_len, wl.heads, wl.d_c, wl.d_rope, wl.d_nope, wl.d_v, wl.block_size,
+                            prob.max_blocks, prob.num_blocks, libmla.MLA_BF16 if wl.dtype == "bf16" else libmla.MLA_F32)
+
+
+def _dt(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+
+def _half_step(ref: np.ndarray, dtype: str) -> np.ndarray:
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126)))
+    return 2.0 ** (e - (8 if dtype == "bf16" else 24))
+
+
+def _round(x64: np.ndarray, dt) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x64)).to(torch.float32).to(dt)
+
+
+def _check_bound(gpu, ref, absprod, K, dtype, what, extra=0.0, exact_frac=None):
+    """|gpu - ref| <= half step + K 2^-24 absprod + extra absprod, element by element."""
+    bound = _half_step(ref, dtype) + (K * 2.0 ** -24 + extra) * absprod
+    bad = np.abs(gpu - ref) > bound
+    say(f"  {what}: {int(bad.sum())} of {bad.size} elements outside the bound")
+    assert not bad.any(), f"{what}: first offender at {np.argwhere(bad)[0]}"
+    if exact_frac is not None and dtype == "bf16":
+        r = to64(_round(ref, torch.bfloat16))
+        frac = float(np.mean(gpu == r))
+        say(f"  {what}: {frac:.4f} equal to the oracle rounded to bf16")
+        assert frac >= exact_frac
+
+
+def _fold_query_ref(w_in64, w_uk64):
+    return orc.fold_query_weight_reference(w_in64, w_uk64)
+
+
+def _absprod_query_fold(w_in64, w_uk64):
+    return np.stack([np.abs(w_uk64[h]).T @ np.abs(w_in64[h]) for h in range(w_in64.shape[0])])
+
+
+def _absprod_output_fold(w_o64, w_uv64):
+    return orc.fold_output_weight_reference(np.abs(w_o64), np.abs(w_uv64))
+
+
+# ------------------------------------------------------------------ folds
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
+@pytest.mark.parametrize("io", [SMALL_IO, RAGGED_IO])
+def test_fold_query_weight(name, io):
+    wl, prob = _problem(name, **(SMALL if name != "tiny_f32" else {}))
+    fi = make_fold_inputs(prob, d_in=io[0], d_out=io[1])
+    say(f"fold_query {name} d_in={fi.d_in}")
+    d, dt = _dims(wl, prob), _dt(wl)
+    out = torch.full((wl.heads, wl.d_c, fi.d_in), float("nan"), dtype=dt, device="cuda")
+    libmla.mla_fold_query_weight(d, fi.d_in, fi.w_in.cuda(), prob.w_uk.cuda(), out)
+    torch.cuda.synchronize()
+    w_in64, w_uk64 = fi.f64("w_in"), prob.f64("w_uk")
+    ref = _fold_query_ref(w_in64, w_uk64)
+    gpu = to64(out)
+    assert_parity(gpu, ref, wl.dtype, "W~_Q")
+    _check_bound(gpu, ref, _absprod_query_fold(w_in64, w_uk64), wl.d_nope, wl.dtype, "W~_Q", exact_frac=0.95)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
+@pytest.mark.parametrize("io", [SMALL_IO, RAGGED_IO])
+def test_fold_output_weight(name, io):
+    wl, prob = _problem(name, **(SMALL if name != "tiny_f32" else {}))
+    fi = make_fold_inputs(prob, d_in=io[0], d_out=io[1])
+    say(f"fold_output {name} d_out={fi.d_out}")
+    d, dt = _dims(wl, prob), _dt(wl)
+    out = torch.full((fi.d_out, wl.heads * wl.d_c), float("nan"), dtype=dt, device="cuda")
+    libmla.mla_fold_output_weight(d, fi.d_out, fi.w_o.cuda(), prob.w_uv.cuda(), out)
+    torch.cuda.synchronize()
+    w_o64, w_uv64 = fi.f64("w_o"), prob.f64("w_uv")
+    ref = orc.fold_output_weight_reference(w_o64, w_uv64)
+    gpu = to64(out)
+    assert_parity(gpu, ref, wl.dtype, "W~^O")
+    _check_bound(gpu, ref, _absprod_output_fold(w_o64, w_uv64), wl.d_v, wl.dtype, "W~^O", exact_frac=0.95)
+
+
+# ------------------------------------------------------------------ products on the oracle's folded weights
+
+def _fused_query(wl, prob, fi, w_fused):
+    d, dt = _dims(wl, prob), _dt(wl)
+    q_cat = torch.full((wl.batch, wl.q_len, wl.heads, wl.d_c + wl.d_rope), float("nan"), dtype=dt, device="cuda")
+    libmla.mla_fused_query(d, fi.d_in, fi.x.cuda(), prob.q_rope.cuda(), w_fused.cuda(), q_cat)
+    torch.cuda.synchronize()
+    return to64(q_cat)
+
+
+def _fused_output(wl, prob, fi, w_fused, d_out=None):
+    d, dt = _dims(wl, prob), _dt(wl)
+    d_out = fi.d_out if d_out is None else d_out
+    nbytes = libmla.mla_fused_output_workspace_bytes(d, d_out)
+    ws = torch.full((max(nbytes, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.full((wl.batch, wl.q_len, d_out), float("nan"), dtype=dt, device="cuda")
+    libmla.mla_fused_output(d, d_out, fi.o.cuda(), w_fused.cuda(), y, ws if nbytes else None)
+    torch.cuda.synchronize()
+    return to64(y)
+
+
+def _check_fused_query(wl, prob, fi, gpu, wf64):
+    x64, qr64 = fi.f64("x"), prob.f64("q_rope")
+    ref = orc.fused_query_reference(x64, qr64, wf64)
+    assert_parity(gpu, ref, wl.dtype, "q_cat (fused)")
+    assert np.array_equal(gpu[..., wl.d_c:], qr64), "the RoPE part must pass through unchanged"
+    absprod = np.stack([np.abs(x64) @ np.abs(wf64[h]).T for h in range(wl.heads)], axis=2)
+    _check_bound(gpu[..., :wl.d_c], ref[..., :wl.d_c], absprod, fi.d_in, wl.dtype, "q_cat (fused)")
+
+
+def _check_fused_output(wl, fi, gpu, wf64, rows=None):
+    o64 = fi.f64("o")
+    if rows is not None:
+        wf64 = wf64[rows]
+        gpu = gpu[..., rows]
+    ref = orc.fused_output_reference(o64, wf64)
+    assert_parity(gpu, ref, wl.dtype, "y (fused)")
+    M = wl.batch * wl.q_len
+    absprod = (np.abs(o64).reshape(M, -1) @ np.abs(wf64).T).reshape(ref.shape)
+    extra = 2.0 ** -17 if wl.dtype == "bf16" else 0.0
+    _check_bound(gpu, ref, absprod, wl.heads * wl.d_c, wl.dtype, "y (fused)", extra=extra)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
+@pytest.mark.parametrize("io", [SMALL_IO, RAGGED_IO])
+@pytest.mark.parametrize("kernels", ["default", "portable"])
+def test_fused_query(name, io, kernels, monkeypatch):
+    wl, prob = _problem(name, **(SMALL if name != "tiny_f32" else {}))
+    fi = make_fold_inputs(prob, d_in=io[0], d_out=io[1])
+    say(f"fused_query {name} d_in={fi.d_in} kernels={kernels}")
+    wf = _round(_fold_query_ref(fi.f64("w_in"), prob.f64("w_uk")), _dt(wl))
+    if kernels == "portable":
+        monkeypatch.setenv("MLA_KERNELS", "portable")
+    gpu = _fused_query(wl, prob, fi, wf)
+    _check_fused_query(wl, prob, fi, gpu, to64(wf))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
+@pytest.mark.parametrize("io", [SMALL_IO, RAGGED_IO])
+@pytest.mark.parametrize("kernels", ["default", "portable"])
+def test_fused_output(name, io, kernels, monkeypatch):
+    wl, prob = _problem(name, **(SMALL if name != "tiny_f32" else {}))
+    fi = make_fold_inputs(prob, d_in=io[0], d_out=io[1])
+    say(f"fused_output {name} d_out={fi.d_out} kernels={kernels}")
+    wf = _round(orc.fold_output_weight_reference(fi.f64("w_o"), prob.f64("w_uv")), _dt(wl))
+    if kernels == "portable":
+        monkeypatch.setenv("MLA_KERNELS", "portable")
+    gpu = _fused_output(wl, prob, fi, wf)
+    _check_fused_output(wl, fi, gpu, to64(wf))
+
+
+@pytest.mark.parametrize("batch,q_len", [(40, 2), (1, 1), (64, 1)])
+def test_fused_row_blocks(batch, q_len):
+    """Row counts of one partial tile, exactly one tile, and more than one tile on the matrix cores."""
+    wl, prob = _problem("single_4k_bf16", **dict(SMALL, batch=batch, q_len=q_len))
+    fi = make_fold_inputs(prob, d_in=SMALL_IO[0], d_out=SMALL_IO[1])
+    say(f"fused row blocks B={batch} Lq={q_len}")
+    wq = _round(_fold_query_ref(fi.f64("w_in"), prob.f64("w_uk")), torch.bfloat16)
+    _check_fused_query(wl, prob, fi, _fused_query(wl, prob, fi, wq), to64(wq))
+    wo = _round(orc.fold_output_weight_reference(fi.f64("w_o"), prob.f64("w_uv")), torch.bfloat16)
+    _check_fused_output(wl, fi, _fused_output(wl, prob, fi, wo), to64(wo))
+
+
+def test_fused_query_without_rope():
+    wl, prob = _problem("single_4k_bf16", **dict(SMALL, d_rope=0))
+    fi = make_fold_inputs(prob, d_in=SMALL_IO[0], d_out=SMALL_IO[1])
+    say("fused_query d_rope=0")
+    wf = _round(_fold_query_ref(fi.f64("w_in"), prob.f64("w_uk")), torch.bfloat16)
+    d = _dims(wl, prob)
+    q_cat = torch.full((wl.batch, wl.q_len, wl.heads, wl.d_c), float("nan"), dtype=torch.bfloat16, device="cuda")
+    libmla.mla_fused_query(d, fi.d_in, fi.x.cuda(), None, wf.cuda(), q_cat)
+    torch.cuda.synchronize()
+    ref = orc.fused_query_reference(fi.f64("x"), np.zeros((wl.batch, wl.q_len, wl.heads, 0)), to64(wf))
+    assert_parity(to64(q_cat), ref, "bf16", "q_cat (fused, no RoPE)")
+
+
+def test_mfma_and_portable_agree_bf16(monkeypatch):
+    """Both kernel families of the fused products meet the same oracle; here they also meet each other."""
+    wl, prob = _problem("single_4k_bf16", **SMALL)
+    fi = make_fold_inputs(prob, d_in=SMALL_IO[0], d_out=SMALL_IO[1])
+    wq = _round(_fold_query_ref(fi.f64("w_in"), prob.f64("w_uk")), torch.bfloat16)
+    wo = _round(orc.fold_output_weight_reference(fi.f64("w_o"), prob.f64("w_uv")), torch.bfloat16)
+    a_q, a_o = _fused_query(wl, prob, fi, wq), _fused_output(wl, prob, fi, wo)
+    monkeypatch.setenv("MLA_KERNELS", "portable")
+    b_q, b_o = _fused_query(wl, prob, fi, wq), _fused_output(wl, prob, fi, wo)
+    monkeypatch.delenv("MLA_KERNELS")
+    # both round once to bf16 from float32 sums in different orders (and y from a float32 o on one side,
+    # its hi + lo split on the other), so they meet each other to the bf16 bar
+    for a, b, what in ((a_q, b_q, "q_cat"), (a_o, b_o, "y")):
+        say(f"  {what}: {float(np.mean(a == b)):.4f} bit-identical between the kernel families")
+        assert_parity(a, b, "bf16", f"{what}: matrix-core vs portable")
+
+
+# ------------------------------------------------------------------ end to end against the unfolded route
+
+@pytest.mark.parametrize("name", ["tiny_f32", "single_4k_bf16"])
+def test_folded_route_equals_unfolded(name):
+    """Library fold + fused product against the oracle's unfolded route (project, absorb, attend-side products)."""
+    wl, prob = _problem(name, **(SMALL if name != "tiny_f32" else {}))
+    fi = make_fold_inputs(prob, d_in=SMALL_IO[0], d_out=SMALL_IO[1])
+    say(f"folded vs unfolded {name}")
+    d, dt = _dims(wl, prob), _dt(wl)
+    wq = torch.empty((wl.heads, wl.d_c, fi.d_in), dtype=dt, device="cuda")
+    libmla.mla_fold_query_weight(d, fi.d_in, fi.w_in.cuda(), prob.w_uk.cuda(), wq)
+    wo = torch.empty((fi.d_out, wl.heads * wl.d_c), dtype=dt, device="cuda")
+    libmla.mla_fold_output_weight(d, fi.d_out, fi.w_o.cuda(), prob.w_uv.cuda(), wo)
+    gq = _fused_query(wl, prob, fi, wq)
+    gy = _fused_output(wl, prob, fi, wo)
+    # the unfolded route: q^C = W_in x per head, then W^UK absorbed; u = W^UV o per head, then W^O
+    q_nope = np.einsum("hnd,bjd->bjhn", fi.f64("w_in"), fi.f64("x"))
+    ref_q = orc.absorb_q_reference(q_nope, prob.f64("q_rope"), prob.f64("w_uk"))
+    u = orc.absorb_out_reference(fi.f64("o"), prob.f64("w_uv"))
+    ref_y = u.reshape(wl.batch, wl.q_len, -1) @ fi.f64("w_o").T
+    assert_parity(gq, ref_q, wl.dtype, "q_cat folded vs unfolded")
+    assert_parity(gy, ref_y, wl.dtype, "y folded vs unfolded")
+
+
+# ------------------------------------------------------------------ full DeepSeek-V3 size (B = 64, H = 128)
+
+FULL = "batch64_1k8k_bf16"
+D_IN, D_OUT = 1536, 7168
+
+
+@pytest.fixture(scope="module")
+def full():
+    wl, prob = _problem(FULL)
+    fi = make_fold_inputs(prob, d_in=D_IN, d_out=D_OUT)
+    return wl, prob, fi
+
+
+def test_full_fold_query_sampled_heads(full):
+    wl, prob, fi = full
+    say("full fold_query")
+    d = _dims(wl, prob)
+    out = torch.empty((wl.heads, wl.d_c, D_IN), dtype=torch.bfloat16, device="cuda")
+    libmla.mla_fold_query_weight(d, D_IN, fi.w_in.cuda(), prob.w_uk.cuda(), out)
+    torch.cuda.synchronize()
+    hs = [0, 45, 77, 127]
+    w_in64, w_uk64 = fi.f64("w_in")[hs], prob.f64("w_uk")[hs]
+    ref = _fold_query_ref(w_in64, w_uk64)
+    gpu = to64(out[hs])
+    assert_parity(gpu, ref, "bf16", "W~_Q (sampled heads)")
+    _check_bound(gpu, ref, _absprod_query_fold(w_in64, w_uk64), wl.d_nope, "bf16", "W~_Q", exact_frac=0.95)
+
+
+def test_full_fold_output_sampled_rows(full):
+    wl, prob, fi = full
+    say("full fold_output")
+    d = _dims(wl, prob)
+    out = torch.empty((D_OUT, wl.heads * wl.d_c), dtype=torch.bfloat16, device="cuda")
+    libmla.mla_fold_output_weight(d, D_OUT, fi.w_o.cuda(), prob.w_uv.cuda(), out)
+    torch.cuda.synchronize()
+    rows = np.random.Generator(np.random.PCG64(11)).choice(D_OUT, 48, replace=False)
+    rows = np.concatenate([rows, [0, D_OUT - 1]])
+    w_o64, w_uv64 = fi.f64("w_o"), prob.f64("w_uv")
+    ref = orc.fold_output_weight_reference(w_o64, w_uv64, rows=rows)
+    gpu = to64(out[torch.from_numpy(rows).cuda()])
+    assert_parity(gpu, ref, "bf16", "W~^O (sampled rows)")
+    absprod = orc.fold_output_weight_reference(np.abs(w_o64), np.abs(w_uv64), rows=rows)
+    _check_bound(gpu, ref, absprod, wl.d_v, "bf16", "W~^O", exact_frac=0.95)
+
+
+def test_full_fused_query(full):
+    wl, prob, fi = full
+    say("full fused_query")
+    wf = _round(_fold_query_ref(fi.f64("w_in"), prob.f64("w_uk")), torch.bfloat16)
+    gpu = _fused_query(wl, prob, fi, wf)
+    _check_fused_query(wl, prob, fi, gpu, to64(wf))
+
+
+def test_full_fused_output_sampled_rows(full):
+    wl, prob, fi = full
+    say("full fused_output (stand-in weight)")
+    wf = synthetic_fused_output_weight(prob, D_OUT)
+    gpu = _fused_output(wl, prob, fi, wf)
+    rows = np.random.Generator(np.random.PCG64(12)).choice(D_OUT, 96, replace=False)
+    rows = np.concatenate([rows, [0, 63, 64, D_OUT - 1]])
+    wf64 = wf[torch.from_numpy(rows)].to(torch.float64).numpy()
+    _check_fused_output(wl, fi, gpu[..., rows], wf64)
+
+
+def test_full_folded_output_route_sampled(full):
+    """Library fold of the full W^O, then the fused product, against W^O (W^UV o) on sampled outputs."""
+    wl, prob, fi = full
+    say("full folded output route")
+    d = _dims(wl, prob)
+    wo = torch.empty((D_OUT, wl.heads * wl.d_c), dtype=torch.bfloat16, device="cuda")
+    libmla.mla_fold_output_weight(d, D_OUT, fi.w_o.cuda(), prob.w_uv.cuda(), wo)
+    gy = _fused_output(wl, prob, fi, wo)
+    rows = np.random.Generator(np.random.PCG64(13)).choice(D_OUT, 64, replace=False)
+    u = orc.absorb_out_reference(fi.f64("o"), prob.f64("w_uv"))
+    ref = u.reshape(wl.batch, wl.q_len, -1) @ fi.f64("w_o")[rows].T
+    assert_parity(gy[..., rows], ref, "bf16", "y folded vs unfolded (sampled)")
