@@ -20,16 +20,16 @@
 // contraction order, one rounding to the output type.
 //
 // Matrix-core runtime path (bf16 weights): Y = X W^T with W [N x K]
-// contiguous along K.  Workgroup (column tile, row block, k-split) multiplies
-// 64 columns by 64 rows over its share of K; its four waves take alternate
-// 64-element chunks of that share and add their four 32 x 32 accumulators
-// through LDS in a fixed order.  Every MFMA operand is one 16-byte load (two
-// for a float32 X) straight from memory: the weight streams from HBM once per
-// row block, X is re-read from L2 by every column tile.  A float32 X (the
-// latent attention output) enters the bf16 MFMAs as hi + lo with hi, lo in
-// bf16, so its rounding error is that of about 16 mantissa bits.  With one
-// split the workgroup writes the bf16 result; with several it writes a float32
-// partial, and a second kernel adds the partials in split order.
+// contiguous along K and at most a few dozen rows of X, so the product is
+// bound by streaming W from HBM.  Workgroup (column block, row block,
+// k-split) owns 128 (query) or 256 (output) columns and 64 rows over its
+// share of K; its four waves own disjoint columns.  X passes through LDS once
+// per workgroup, W goes straight from memory into the MFMA operands through a
+// three-chunk register ring.  A float32 X (the latent attention output) enters
+// the bf16 MFMAs as hi + lo with hi, lo in bf16, so its rounding error is that
+// of about 16 mantissa bits.  With one split the workgroup writes the bf16
+// result; with several it writes a float32 partial, and a second kernel adds
+// the partials in split order.
 #include <type_traits>
 
 #include "common.h"
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kThreads) void pass_rope(const T* __restrict__ q_ro
 }
 
 // ------------------------------------------------------------------ matrix-core linear
-constexpr int kLChunk = 64;  // contraction elements per wave and chunk (four MFMA steps)
-constexpr int kLTile = 64;   // output columns and rows per workgroup
+constexpr int kLChunk = 64;  // contraction elements per chunk (four MFMA steps)
+constexpr int kLRows = 64;   // rows per workgroup (two 32-row MFMA tiles)
 constexpr int kLMaxKSplit = 16;
 
 // Where output (m, n) goes: Y[m * ldy + (n / gs) * gstride + n % gs].  With
@@ -136,160 +136,214 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
                     (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16));
 }
 
-// hi + lo split of eight floats (two 16-byte loads) into two bf16x8 operands
-__device__ __forceinline__ void split_hilo(const uint4& p, const uint4& q, bf16x8& hi, bf16x8& lo) {
+// hi + lo split of eight floats into two 16-byte groups of bf16
+__device__ __forceinline__ void split_hilo(const uint4& p, const uint4& q, uint4& hi, uint4& lo) {
   const float x[8] = {__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z), __uint_as_float(p.w),
                       __uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w)};
-  uint16_t h[8], l[8];
+  uint32_t h[8], l[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     h[e] = f32_to_bf16_bits(x[e]);
-    l[e] = f32_to_bf16_bits(x[e] - bf16_bits_to_f32(h[e]));
+    l[e] = f32_to_bf16_bits(x[e] - bf16_bits_to_f32((uint16_t)h[e]));
   }
-  const uint4 hu = make_uint4(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16, h[4] | (uint32_t)h[5] << 16,
-                              h[6] | (uint32_t)h[7] << 16);
-  const uint4 lu = make_uint4(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16, l[4] | (uint32_t)l[5] << 16,
-                              l[6] | (uint32_t)l[7] << 16);
-  hi = __builtin_bit_cast(bf16x8, hu);
-  lo = __builtin_bit_cast(bf16x8, lu);
+  hi = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
+  lo = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16);
 }
 
-// One-dimensional grid of column tiles x row blocks x k-splits, split-major
-// in the XCD-local order, so that the workgroups reading one split's slice of
-// X mostly share an XCD and its L2.  MFMA step s of chunk c takes K elements
-// 64 c + 16 s .. + 15; the lane with half hi = lane >> 5 supplies 8 hi .. 8 hi
-// + 7 of them from its W row (A operand, output column n = lane & 31 of the
-// column tile) and of its X row (B operand, output row m = lane & 31 of the
-// row tile).
-template <bool XF32>
+// Columns per workgroup: four waves, each owning CT 32-column MFMA tiles.
+template <int CT> constexpr int linear_block() { return 4 * 32 * CT; }
+
+// step(R, c + R) for R = 0, 1, ... while R < RING and c + R < c_hi, with R a
+// compile-time constant (so that register-ring slots are static).
+template <int R, int RING, typename F>
+__device__ __forceinline__ void ring_steps(F& step, int c, int c_hi) {
+  if constexpr (R < RING) {
+    if (c + R < c_hi) {
+      step(std::integral_constant<int, R>{}, c + R);
+      ring_steps<R + 1, RING>(step, c, c_hi);
+    }
+  }
+}
+
+// step(R, c + R) for every R < RING, unconditionally.
+template <int R, int RING, typename F>
+__device__ __forceinline__ void ring_steps_all(F& step, int c) {
+  if constexpr (R < RING) {
+    step(std::integral_constant<int, R>{}, c + R);
+    ring_steps_all<R + 1, RING>(step, c);
+  }
+}
+
+// One-dimensional grid of column blocks x row blocks x k-splits, split-major
+// in the XCD-local order.  Each wave owns CT column tiles and both row tiles
+// of its workgroup over the workgroup's whole share of K, so no partial sums
+// cross waves.  Per 64-element chunk the workgroup stages X (64 rows) in LDS
+// once, as bf16 (hi and lo planes for a float32 X), and every wave reads its
+// B operands there; the W operands (A: output column n = lane & 31 of a
+// tile, K elements 16 s + 8 hi .. + 7 of step s, hi = lane >> 5) stream
+// straight from memory into a ring of RING chunks, RING - 1 chunks ahead of
+// the MFMAs.  X for the next chunk is requested before the ring's newest W chunk,
+// so writing it to LDS never waits for that W chunk.
+//
+// LDS row of a plane: 64 bf16 = eight 16-byte groups, group j of row m kept
+// at slot j ^ (m & 7) so that the 32 rows read by one MFMA operand load fall
+// on distinct banks.
+template <bool XF32, int CT, int RING>
 __global__ __launch_bounds__(kThreads) void linear_mfma(const void* __restrict__ Xv, const uint16_t* __restrict__ W,
                                                         float* __restrict__ part, LinearOut out, int M, int N, int K,
                                                         int per, int ks) {
-  __shared__ float4 red[kThreads / 64][16][64];  // [wave][4 tile + group][lane], 64 KiB
+  constexpr int kPlanes = XF32 ? 2 : 1;
+  constexpr int kBlock = linear_block<CT>();
+  constexpr int kXLoads = XF32 ? 4 : 2;  // 16-byte X loads per thread and chunk
+  __shared__ __align__(16) uint8_t xs[2][kPlanes][kLRows * 128];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
-  const int ntiles = N / kLTile, per_split = ntiles * ((M + kLTile - 1) / kLTile);
+  const int nblocks = N / kBlock, per_split = nblocks * ((M + kLRows - 1) / kLRows);
   const int L = xcd_local_index(blockIdx.x, gridDim.x);
   const int ky = L / per_split, rest = L - ky * per_split;
-  const int n0 = (rest % ntiles) * kLTile, mbase = (rest / ntiles) * kLTile;
+  const int n0 = (rest % nblocks) * kBlock, mbase = (rest / nblocks) * kLRows;
   const int nch = K / kLChunk;
-  const int c_hi = min(nch, (ky + 1) * per);
+  const int c_lo = ky * per, c_hi = min(nch, c_lo + per);
+  const int nw = n0 + wave * 32 * CT;  // this wave's first column
 
-  const uint16_t* w0 = W + (size_t)(n0 + (lane & 31)) * K + 8 * hi;
-  const uint16_t* w1 = w0 + (size_t)32 * K;
-  const size_t xr0 = (size_t)min(mbase + (lane & 31), M - 1) * K + 8 * hi;
-  const size_t xr1 = (size_t)min(mbase + 32 + (lane & 31), M - 1) * K + 8 * hi;
-  constexpr int kXLoads = XF32 ? 2 : 1;  // 16-byte loads per X operand
-
-  f32x16 acc[2][2] = {};  // [row tile][column tile]
-  uint4 wa[2][4], xa[2][4 * kXLoads];
-  auto load = [&](int c, uint4(&w)[2][4], uint4(&x)[2][4 * kXLoads]) {
-    const size_t o = (size_t)c * kLChunk;
+  const uint16_t* wrow[CT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      w[0][s] = *reinterpret_cast<const uint4*>(w0 + o + 16 * s);
-      w[1][s] = *reinterpret_cast<const uint4*>(w1 + o + 16 * s);
-    }
+  for (int u = 0; u < CT; ++u) wrow[u] = W + (size_t)(nw + 32 * u + (lane & 31)) * K + 8 * hi;
+
+  // X staging: thread tid covers 8-element groups g = tid and tid + 256 of
+  // the chunk (row g >> 3, group g & 7)
+  auto x_src = [&](int q) -> size_t {
+    const int g = tid + kThreads * q;
+    return (size_t)min(mbase + (g >> 3), M - 1) * K + 8 * (g & 7);
+  };
+  const size_t xo0 = x_src(0), xo1 = x_src(1);
+  auto lds_slot = [](int m, int j) { return m * 128 + ((j ^ (m & 7)) << 4); };
+  const int st0 = lds_slot(tid >> 3, tid & 7), st1 = lds_slot((tid + kThreads) >> 3, tid & 7);
+
+  struct XStage {
+    uint4 v[kXLoads];
+  };
+  auto load_x = [&](int c) {
+    XStage xs_;
+    uint4* xg = xs_.v;
+    const size_t o = (size_t)c * kLChunk;
     if constexpr (XF32) {
       const float* X = static_cast<const float*>(Xv);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        x[0][2 * s] = *reinterpret_cast<const uint4*>(X + xr0 + o + 16 * s);
-        x[0][2 * s + 1] = *reinterpret_cast<const uint4*>(X + xr0 + o + 16 * s + 4);
-        x[1][2 * s] = *reinterpret_cast<const uint4*>(X + xr1 + o + 16 * s);
-        x[1][2 * s + 1] = *reinterpret_cast<const uint4*>(X + xr1 + o + 16 * s + 4);
-      }
+      xg[0] = *reinterpret_cast<const uint4*>(X + xo0 + o);
+      xg[1] = *reinterpret_cast<const uint4*>(X + xo0 + o + 4);
+      xg[2] = *reinterpret_cast<const uint4*>(X + xo1 + o);
+      xg[3] = *reinterpret_cast<const uint4*>(X + xo1 + o + 4);
     } else {
       const uint16_t* X = static_cast<const uint16_t*>(Xv);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        x[0][s] = *reinterpret_cast<const uint4*>(X + xr0 + o + 16 * s);
-        x[1][s] = *reinterpret_cast<const uint4*>(X + xr1 + o + 16 * s);
-      }
+      xg[0] = *reinterpret_cast<const uint4*>(X + xo0 + o);
+      xg[1] = *reinterpret_cast<const uint4*>(X + xo1 + o);
+    }
+    return xs_;
+  };
+  auto store_x = [&](int buf, const XStage& st) {
+    const uint4* xg = st.v;
+    if constexpr (XF32) {
+      uint4 h0, l0, h1, l1;
+      split_hilo(xg[0], xg[1], h0, l0);
+      split_hilo(xg[2], xg[3], h1, l1);
+      *reinterpret_cast<uint4*>(&xs[buf][0][st0]) = h0;
+      *reinterpret_cast<uint4*>(&xs[buf][1][st0]) = l0;
+      *reinterpret_cast<uint4*>(&xs[buf][0][st1]) = h1;
+      *reinterpret_cast<uint4*>(&xs[buf][1][st1]) = l1;
+    } else {
+      *reinterpret_cast<uint4*>(&xs[buf][0][st0]) = xg[0];
+      *reinterpret_cast<uint4*>(&xs[buf][0][st1]) = xg[1];
     }
   };
-  int c = ky * per + wave;
-  if (c < c_hi) load(c, wa, xa);
-  while (c < c_hi) {
-    const int cn = c + kThreads / 64;
-    uint4 wb[2][4], xb[2][4 * kXLoads];
-    if (cn < c_hi) load(cn, wb, xb);
+  auto load_w = [&](int c, uint4(&w)[CT][4]) {
+    const size_t o = (size_t)c * kLChunk;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int u = 0; u < CT; ++u) w[u][s] = *reinterpret_cast<const uint4*>(wrow[u] + o + 16 * s);
+  };
+
+  f32x16 acc[2][CT];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < CT; ++u) acc[t][u] = f32x16{};
+  auto compute = [&](int buf, const uint4(&w)[CT][4]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        const int slot = lds_slot(32 * t + (lane & 31), 2 * s + hi);
+        const bf16x8 xh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&xs[buf][0][slot]));
+#pragma unroll
+        for (int u = 0; u < CT; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[u][s]), xh, acc[t][u], 0,
+                                                              0, 0);
         if constexpr (XF32) {
-          bf16x8 xh, xl;
-          split_hilo(xa[t][2 * s], xa[t][2 * s + 1], xh, xl);
+          const bf16x8 xl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&xs[buf][1][slot]));
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 wv = __builtin_bit_cast(bf16x8, wa[u][s]);
-            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xh, acc[t][u], 0, 0, 0);
-            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xl, acc[t][u], 0, 0, 0);
-          }
-        } else {
-          const bf16x8 xv = __builtin_bit_cast(bf16x8, xa[t][s]);
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wa[u][s]), xv, acc[t][u],
+          for (int u = 0; u < CT; ++u)
+            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w[u][s]), xl, acc[t][u],
                                                                 0, 0, 0);
         }
       }
     }
-    if (cn >= c_hi) break;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) wa[u][s] = wb[u][s];
-#pragma unroll
-      for (int s = 0; s < 4 * kXLoads; ++s) xa[u][s] = xb[u][s];
-    }
-    c = cn;
-  }
+  };
 
-  // accumulator element r of lane (m = lane & 31, hi) is output column
-  // 8 (r >> 2) + 4 hi + (r & 3) of its column tile
+  // Loads past the workgroup's last chunk re-read that chunk (an L2 hit), so
+  // that no load sits under a branch and the compiler's wait counts stay
+  // exact across the loop.
+  uint4 wr[RING][CT][4];
+  if (c_lo < c_hi) {
+    const XStage x0 = load_x(c_lo);
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        red[wave][(2 * t + u) * 4 + g][lane] =
-            make_float4(acc[t][u][4 * g], acc[t][u][4 * g + 1], acc[t][u][4 * g + 2], acc[t][u][4 * g + 3]);
+    for (int r = 0; r + 1 < RING; ++r) load_w(min(c_lo + r, c_hi - 1), wr[r]);
+    store_x(0, x0);
+  }
   __syncthreads();
-  // wave w adds up tile w: row tile w >> 1, column tile w & 1
-  const int m = mbase + 32 * (wave >> 1) + (lane & 31);
+  auto step = [&](auto R, int cc) {
+    constexpr int r = decltype(R)::value;
+    const XStage xn = load_x(min(cc + 1, c_hi - 1));
+    load_w(min(cc + RING - 1, c_hi - 1), wr[(r + RING - 1) % RING]);
+    compute((cc - c_lo) & 1, wr[r]);
+    store_x((cc + 1 - c_lo) & 1, xn);  // that buffer was last read before the previous barrier
+    __syncthreads();
+  };
+  int c = c_lo;
+  for (; c + RING <= c_hi; c += RING) ring_steps_all<0, RING>(step, c);
+  ring_steps<0, RING>(step, c, c_hi);
+
+  // accumulator element r of lane (m = lane & 31, hi) is column
+  // 8 (r >> 2) + 4 hi + (r & 3) of its tile
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int q = 4 * wave + g;
-    float4 sum = red[0][q][lane];
-#pragma unroll
-    for (int v = 1; v < kThreads / 64; ++v) {
-      const float4 x = red[v][q][lane];
-      sum.x += x.x;
-      sum.y += x.y;
-      sum.z += x.z;
-      sum.w += x.w;
-    }
-    const int n = n0 + 32 * (wave & 1) + 8 * g + 4 * hi;
+  for (int t = 0; t < 2; ++t) {
+    const int m = mbase + 32 * t + (lane & 31);
     if (m >= M) continue;
-    if (ks == 1) {
-      const int grp = n / out.gs;
-      *reinterpret_cast<uint2*>(out.y + m * out.ldy + (int64_t)grp * out.gstride + (n - grp * out.gs)) =
-          pack_bf16x4(sum.x, sum.y, sum.z, sum.w);
-    } else {
-      *reinterpret_cast<float4*>(part + ((size_t)ky * M + m) * N + n) = sum;
-    }
+#pragma unroll
+    for (int u = 0; u < CT; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = nw + 32 * u + 8 * g + 4 * hi;
+        const f32x16& a = acc[t][u];
+        if (ks == 1) {
+          const int grp = n / out.gs;
+          *reinterpret_cast<uint2*>(out.y + m * out.ldy + (int64_t)grp * out.gstride + (n - grp * out.gs)) =
+              pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        } else {
+          *reinterpret_cast<float4*>(part + ((size_t)ky * M + m) * N + n) =
+              make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+        }
+      }
   }
 
-  // the tail of each group starting in this column tile (split 0 only)
-  if (out.tail != nullptr && ky == 0 && n0 % out.gs == 0) {
-    const int grp = n0 / out.gs;
-    for (int e = tid; e < kLTile * out.d_t; e += kThreads) {
-      const int mm = mbase + e / out.d_t, t = e % out.d_t;
-      if (mm < M) out.y[mm * out.ldy + (int64_t)grp * out.gstride + out.gs + t] =
-          out.tail[((int64_t)mm * out.groups + grp) * out.d_t + t];
-    }
+  // the tails of the groups starting in this column block (split 0 only)
+  if (out.tail != nullptr && ky == 0) {
+    for (int grp = (n0 + out.gs - 1) / out.gs; grp < out.groups && grp * out.gs < n0 + kBlock; ++grp)
+      for (int e = tid; e < kLRows * out.d_t; e += kThreads) {
+        const int mm = mbase + e / out.d_t, t = e % out.d_t;
+        if (mm < M)
+          out.y[mm * out.ldy + (int64_t)grp * out.gstride + out.gs + t] =
+              out.tail[((int64_t)mm * out.groups + grp) * out.d_t + t];
+      }
   }
 }
 
@@ -330,13 +384,13 @@ hipError_t gemm(const TA* A, GemmView a, const TB* Bm, GemmView b, TC* C, GemmVi
 
 int linear_max_ksplit() { return kLMaxKSplit; }
 
-// Split count for the matrix-core linear: as many splits as keep the grid
-// within two workgroups per compute unit (at least one, at most
-// kLMaxKSplit and max_ks, no empty split).
-int linear_ksplit(int M, int N, int K, int cus, int max_ks, int* per_out) {
-  const int64_t tiles = (int64_t)(N / kLTile) * ((M + kLTile - 1) / kLTile);
+// Split count for the matrix-core linear with column blocks of `block`:
+// as many splits as keep the grid within `slots` workgroups per compute unit
+// (at least one, at most kLMaxKSplit and max_ks, no empty split).
+int linear_ksplit(int M, int N, int K, int block, int slots, int cus, int max_ks, int* per_out) {
+  const int64_t tiles = (int64_t)(N / block) * ((M + kLRows - 1) / kLRows);
   const int nch = K / kLChunk;
-  int64_t ks = (2 * (int64_t)cus) / tiles;
+  int64_t ks = ((int64_t)slots * cus) / tiles;
   if (ks < 1) ks = 1;
   if (ks > kLMaxKSplit) ks = kLMaxKSplit;
   if (ks > max_ks) ks = max_ks;
@@ -346,12 +400,19 @@ int linear_ksplit(int M, int N, int K, int cus, int max_ks, int* per_out) {
   return (nch + per - 1) / per;
 }
 
+// query: one 32-column tile per wave and a three-chunk ring (ks = 1 keeps the
+// grid full); output: two tiles per wave (fewer re-reads of the float32
+// latent output) and a four-chunk ring, two workgroups per compute unit.
+constexpr int kQueryCT = 1, kQueryRing = 3, kOutputCT = 2, kOutputRing = 4, kOutputSlots = 2;
+
 bool fused_query_mfma_supported(const mla_dims& d, int d_in) {
-  return d.dtype == MLA_BF16 && d_in % kLChunk == 0 && d.d_c % kLTile == 0;
+  return d.dtype == MLA_BF16 && d_in % kLChunk == 0 &&
+         ((int64_t)d.num_heads * d.d_c) % linear_block<kQueryCT>() == 0;
 }
 
 bool fused_output_mfma_supported(const mla_dims& d, int d_out) {
-  return d.dtype == MLA_BF16 && ((int64_t)d.num_heads * d.d_c) % kLChunk == 0 && d_out % kLTile == 0;
+  return d.dtype == MLA_BF16 && ((int64_t)d.num_heads * d.d_c) % kLChunk == 0 &&
+         d_out % linear_block<kOutputCT>() == 0;
 }
 
 hipError_t launch_fold_query(const mla_dims& d, int d_in, const void* w_in, const void* w_uk, void* w_fused,
@@ -387,11 +448,11 @@ hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* 
   if (mfma) {
     const int N = d.num_heads * d.d_c;
     int per = 0;
-    const int ks = linear_ksplit(M, N, d_in, cus, 1, &per);
+    const int ks = linear_ksplit(M, N, d_in, linear_block<kQueryCT>(), 2, cus, 1, &per);
     const LinearOut out{static_cast<uint16_t*>(q_cat), (int64_t)d.num_heads * D, d.d_c, D,
                         d.d_rope > 0 ? static_cast<const uint16_t*>(q_rope) : nullptr, d.d_rope, d.num_heads};
-    const int blocks = (N / kLTile) * ((M + kLTile - 1) / kLTile) * ks;
-    hipLaunchKernelGGL(linear_mfma<false>, dim3(blocks), dim3(kThreads), 0, stream, x,
+    const int blocks = (N / linear_block<kQueryCT>()) * ((M + kLRows - 1) / kLRows) * ks;
+    hipLaunchKernelGGL((linear_mfma<false, kQueryCT, kQueryRing>), dim3(blocks), dim3(kThreads), 0, stream, x,
                        static_cast<const uint16_t*>(w_fused), nullptr, out, M, N, d_in, per, ks);
     return hipGetLastError();
   }
@@ -422,10 +483,10 @@ hipError_t launch_fused_output(const mla_dims& d, int d_out, int cus, const floa
   const int M = d.batch * d.q_len, K = d.num_heads * d.d_c;
   if (mfma) {
     int per = 0;
-    const int ks = linear_ksplit(M, d_out, K, cus, kLMaxKSplit, &per);
+    const int ks = linear_ksplit(M, d_out, K, linear_block<kOutputCT>(), kOutputSlots, cus, kLMaxKSplit, &per);
     const LinearOut out{static_cast<uint16_t*>(y), d_out, d_out, 0, nullptr, 0, 1};
-    const int blocks = (d_out / kLTile) * ((M + kLTile - 1) / kLTile) * ks;
-    hipLaunchKernelGGL(linear_mfma<true>, dim3(blocks), dim3(kThreads), 0, stream, o,
+    const int blocks = (d_out / linear_block<kOutputCT>()) * ((M + kLRows - 1) / kLRows) * ks;
+    hipLaunchKernelGGL((linear_mfma<true, kOutputCT, kOutputRing>), dim3(blocks), dim3(kThreads), 0, stream, o,
                        static_cast<const uint16_t*>(w_fused), ws, out, M, d_out, K, per, ks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ks == 1) return e;

@@ -79,7 +79,7 @@ hipError_t launch_fold_output(const mla_dims& d, int d_out, const void* w_o, con
 bool fused_query_mfma_supported(const mla_dims& d, int d_in);
 bool fused_output_mfma_supported(const mla_dims& d, int d_out);
 int linear_max_ksplit();
-int linear_ksplit(int M, int N, int K, int cus, int max_ks, int* per_out);
+int linear_ksplit(int M, int N, int K, int block, int slots, int cus, int max_ks, int* per_out);
 hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* x, const void* q_rope,
                               const void* w_fused, void* q_cat, bool mfma, hipStream_t stream);
 hipError_t launch_fused_output(const mla_dims& d, int d_out, int cus, const float* o, const void* w_fused, void* y,

@@ -36,7 +36,7 @@ def _gpu():
 
 # small shapes: several MFMA tiles and split-K chunks, rows that fill no tile
 SMALL = dict(heads=8, d_c=128, d_rope=64, d_nope=32, d_v=48, lengths=("fixed", (64, 64, 64)), batch=3, q_len=2)
-SMALL_IO = (192, 320)  # d_in, d_out: both on the matrix cores for bf16
+SMALL_IO = (192, 512)  # d_in, d_out: both on the matrix cores for bf16
 RAGGED_IO = (100, 100)  # neither a multiple of 64: portable kernels
 
 
