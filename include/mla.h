@@ -301,14 +301,37 @@ int mla_prefill(const mla_dims* dims, int32_t total_tokens, int32_t max_seqlen, 
 
 /* ---- offline weight folds: the steps on either side of the path -------- */
 
+/* Fused weight storage.  A fused weight viewed as a matrix W [N x K] (N its
+ * output columns, K the contraction: W~_Q as [H*d_c x d_in], W~^O as
+ * [d_out x H*d_c]) is stored row-major, except where the matrix-core
+ * products serve its shape (mla_fused_query_weight_packed() /
+ * mla_fused_output_weight_packed() return 1): there it is stored in MFMA
+ * fragment order, an array [N/32][K/64][4][2][32][8] over (32-row tile,
+ * 64-element chunk, step, half, row in tile, element), element (n, k) at
+ *   ((n/32)*(K/64) + k/64)*2048 + ((k%64)/16)*512 + (((k%16)/8)*32 + n%32)*8 + k%8
+ * so that the products stream it in contiguous 1 KiB pieces.  The folds
+ * write, and both products read, whichever order applies; the element count
+ * is the same either way.  A weight made elsewhere must be put in that order
+ * before it is passed to a product. */
+
+/* 1 if the fused query weight for these dims and d_in is stored in fragment
+ * order (bf16, d_in % 64 == 0, H*d_c % 128 == 0), else 0 (also for invalid
+ * arguments).  Host only. */
+int mla_fused_query_weight_packed(const mla_dims* dims, int32_t d_in);
+
+/* 1 if the fused output weight for these dims and d_out is stored in
+ * fragment order (bf16, H*d_c % 64 == 0, d_out % 256 == 0), else 0.  Host
+ * only. */
+int mla_fused_output_weight_packed(const mla_dims* dims, int32_t d_out);
+
 /* Fold W^UK into the query projection ("Deconstructing DeepSeek V4 Pro",
  * Practical Deployment, the fused query weight; "DeepSeek-V3 MLA: Multi-Head
  * Latent Attention Guide", Matrix Absorption Trick section 2):
  *   w_fused[h,c,i] = sum_n w_uk[h,n,c] * w_in[h,n,i]
  * where w_in [H,d_nope,d_in] is the per-head content query projection (a
  * Linear weight of shape (H*d_nope) x d_in, e.g. the query up-projection of a
- * d_in = 1536 query latent), w_uk [H,d_nope,d_c] and w_fused [H,d_c,d_in], all
- * in the storage type.  Float32 accumulation in order of n, one rounding.
+ * d_in = 1536 query latent), w_uk [H,d_nope,d_c] and w_fused [H,d_c,d_in]
+ * (in the fused weight storage order above), all in the storage type.  Float32 accumulation in order of n, one rounding.
  * Offline: run once per weight set.  Uses num_heads, d_c, d_nope and dtype of
  * dims (the other fields must still be valid).  d_in in [1, 65536]. */
 int mla_fold_query_weight(const mla_dims* dims, int32_t d_in, const void* w_in, const void* w_uk, void* w_fused,
@@ -320,9 +343,10 @@ int mla_fold_query_weight(const mla_dims* dims, int32_t d_in, const void* w_in, 
  *   q_cat[b,j,h, d_c:d_c+d_r] = q_rope[b,j,h,:]
  * which equals mla_absorb_q of q_nope[b,j,h] = w_in[h] x[b,j] up to rounding.
  * x [B,Lq,d_in], q_rope [B,Lq,H,d_rope] (NULL if d_rope = 0), w_fused
- * [H,d_c,d_in], q_cat [B,Lq,H,d_c+d_rope], all in the storage type.  Float32
- * accumulation, one rounding.  bf16 with d_in % 64 == 0 and d_c % 64 == 0 runs
- * on the matrix cores; other supported shapes on a portable kernel. */
+ * [H,d_c,d_in] in the fused weight storage order, q_cat [B,Lq,H,d_c+d_rope],
+ * all in the storage type.  Float32 accumulation, one rounding.  Where the
+ * weight is in fragment order the product runs on the matrix cores; other
+ * supported shapes run on a portable kernel. */
 int mla_fused_query(const mla_dims* dims, int32_t d_in, const void* x, const void* q_rope, const void* w_fused,
                     void* q_cat, void* stream);
 
@@ -331,7 +355,8 @@ int mla_fused_query(const mla_dims* dims, int32_t d_in, const void* x, const voi
  * Trick section 3, W~^O):
  *   w_fused[r, h*d_c + c] = sum_v w_o[r, h*d_v + v] * w_uv[h,v,c]
  * w_o [d_out, H*d_v] (W^O acting on the heads' outputs concatenated in head
- * order), w_uv [H,d_v,d_c], w_fused [d_out, H*d_c], all in the storage type.
+ * order), w_uv [H,d_v,d_c], w_fused [d_out, H*d_c] (in the fused weight
+ * storage order above), all in the storage type.
  * Float32 accumulation in order of v, one rounding.  Offline.  Uses
  * num_heads, d_c, d_v and dtype of dims.  d_out in [1, 65536]. */
 int mla_fold_output_weight(const mla_dims* dims, int32_t d_out, const void* w_o, const void* w_uv, void* w_fused,
@@ -347,12 +372,13 @@ int mla_fused_output_workspace_bytes(const mla_dims* dims, int32_t d_out, size_t
  *   y[b,j,r] = sum_{h,c} w_fused[r, h*d_c + c] * o_latent[b,j,h,c]
  * which equals W^O applied to the concatenated mla_absorb_out result up to
  * rounding.  o_latent [B,Lq,H,d_c] float32 (as mla_combine writes it),
- * w_fused [d_out, H*d_c] storage type, y [B,Lq,d_out] storage type; workspace
- * at least mla_fused_output_workspace_bytes() bytes, contents on entry
- * irrelevant.  Float32 accumulation; on the matrix cores (bf16, H*d_c % 64 ==
- * 0, d_out % 64 == 0) o_latent enters as a bf16 hi + lo pair and the split of
- * H*d_c, and so the order of the float32 additions, follows the device's
- * compute-unit count: reproducible on one device type. */
+ * w_fused [d_out, H*d_c] storage type in the fused weight storage order, y
+ * [B,Lq,d_out] storage type; workspace at least
+ * mla_fused_output_workspace_bytes() bytes, contents on entry irrelevant.
+ * Float32 accumulation; on the matrix cores (where the weight is in fragment
+ * order) o_latent enters as a bf16 hi + lo pair and the split of H*d_c, and
+ * so the order of the float32 additions, follows the device's compute-unit
+ * count: reproducible on one device type. */
 int mla_fused_output(const mla_dims* dims, int32_t d_out, const float* o_latent, const void* w_fused, void* y,
                      void* workspace, size_t workspace_bytes, void* stream);
 

@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
         "mla_fold_output_weight": [D, I32, P, P, P, P],
         "mla_fused_output_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_fused_output": [D, I32, P, P, P, P, SZ, P],
+        "mla_fused_query_weight_packed": [D, I32],
+        "mla_fused_output_weight_packed": [D, I32],
         "mla_version": [],
     }
     for name, args in sig.items():
@@ -356,6 +358,14 @@ def mla_fold_output_weight(dims, d_out, w_o, w_uv, w_fused, stream=None):
         ctypes.byref(d), int(d_out), _ptr(w_o, "w_o", st, d_out * H * d.d_v),
         _ptr(w_uv, "w_uv", st, H * d.d_v * d.d_c), _ptr(w_fused, "w_fused", st, d_out * H * d.d_c),
         _stream(stream)))
+
+
+def mla_fused_query_weight_packed(dims, d_in) -> bool:
+    return bool(load().mla_fused_query_weight_packed(ctypes.byref(dims), int(d_in)))
+
+
+def mla_fused_output_weight_packed(dims, d_out) -> bool:
+    return bool(load().mla_fused_output_weight_packed(ctypes.byref(dims), int(d_out)))
 
 
 def mla_fused_output_workspace_bytes(dims, d_out: int) -> int:

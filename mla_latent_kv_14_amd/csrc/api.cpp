@@ -440,7 +440,8 @@ int mla_fold_query_weight(const mla_dims* d, int32_t d_in, const void* w_in, con
   if (st != MLA_OK) return st;
   if (d_in < 1 || d_in > kMaxDModel) return MLA_ERR_INVALID_ARG;
   if (!ptr_ok(w_in) || !ptr_ok(w_uk) || !ptr_ok(w_fused)) return MLA_ERR_INVALID_ARG;
-  return to_status(mla::launch_fold_query(*d, d_in, w_in, w_uk, w_fused, (hipStream_t)stream));
+  return to_status(mla::launch_fold_query(*d, d_in, w_in, w_uk, w_fused, mla::fused_query_mfma_supported(*d, d_in),
+                                          (hipStream_t)stream));
 }
 
 int mla_fused_query(const mla_dims* d, int32_t d_in, const void* x, const void* q_rope, const void* w_fused,
@@ -450,10 +451,12 @@ int mla_fused_query(const mla_dims* d, int32_t d_in, const void* x, const void* 
   if (d_in < 1 || d_in > kMaxDModel) return MLA_ERR_INVALID_ARG;
   if (!ptr_ok(x) || !ptr_ok(w_fused) || !ptr_ok(q_cat) || (d->d_rope > 0 && !ptr_ok(q_rope)))
     return MLA_ERR_INVALID_ARG;
-  const bool mfma = !force_generic() && mla::fused_query_mfma_supported(*d, d_in);
+  const bool packed = mla::fused_query_mfma_supported(*d, d_in);
+  const bool mfma = packed && !force_generic();
   int cus = 1;
   if (mfma && (st = device_cus(&cus)) != MLA_OK) return st;
-  return to_status(mla::launch_fused_query(*d, d_in, cus, x, q_rope, w_fused, q_cat, mfma, (hipStream_t)stream));
+  return to_status(
+      mla::launch_fused_query(*d, d_in, cus, x, q_rope, w_fused, q_cat, mfma, packed, (hipStream_t)stream));
 }
 
 int mla_fold_output_weight(const mla_dims* d, int32_t d_out, const void* w_o, const void* w_uv, void* w_fused,
@@ -462,7 +465,8 @@ int mla_fold_output_weight(const mla_dims* d, int32_t d_out, const void* w_o, co
   if (st != MLA_OK) return st;
   if (d_out < 1 || d_out > kMaxDModel) return MLA_ERR_INVALID_ARG;
   if (!ptr_ok(w_o) || !ptr_ok(w_uv) || !ptr_ok(w_fused)) return MLA_ERR_INVALID_ARG;
-  return to_status(mla::launch_fold_output(*d, d_out, w_o, w_uv, w_fused, (hipStream_t)stream));
+  return to_status(mla::launch_fold_output(*d, d_out, w_o, w_uv, w_fused,
+                                           mla::fused_output_mfma_supported(*d, d_out), (hipStream_t)stream));
 }
 
 int mla_fused_output_workspace_bytes(const mla_dims* d, int32_t d_out, size_t* bytes) {
@@ -485,11 +489,22 @@ int mla_fused_output(const mla_dims* d, int32_t d_out, const float* o_latent, co
   size_t need = 0;
   mla_fused_output_workspace_bytes(d, d_out, &need);
   if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need)) return MLA_ERR_INVALID_ARG;
-  const bool mfma = !force_generic() && mla::fused_output_mfma_supported(*d, d_out);
+  const bool packed = mla::fused_output_mfma_supported(*d, d_out);
+  const bool mfma = packed && !force_generic();
   int cus = 1;
   if (mfma && (st = device_cus(&cus)) != MLA_OK) return st;
   return to_status(mla::launch_fused_output(*d, d_out, cus, o_latent, w_fused, y, static_cast<float*>(workspace),
-                                            mfma, (hipStream_t)stream));
+                                            mfma, packed, (hipStream_t)stream));
+}
+
+int mla_fused_query_weight_packed(const mla_dims* d, int32_t d_in) {
+  if (check_dims(d) != MLA_OK || d_in < 1 || d_in > kMaxDModel) return 0;
+  return mla::fused_query_mfma_supported(*d, d_in) ? 1 : 0;
+}
+
+int mla_fused_output_weight_packed(const mla_dims* d, int32_t d_out) {
+  if (check_dims(d) != MLA_OK || d_out < 1 || d_out > kMaxDModel) return 0;
+  return mla::fused_output_mfma_supported(*d, d_out) ? 1 : 0;
 }
 
 int mla_combine_absorb_out_fused(const mla_dims* d, int32_t num_splits) {

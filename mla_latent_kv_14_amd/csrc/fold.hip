@@ -39,11 +39,33 @@ namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ packed weight order
+// A fused weight viewed as W [N x K] (N output columns, K the contraction) is
+// stored, when the matrix-core path serves its shape, in MFMA fragment order:
+// a [N/32][K/64][4][2][32][8] array over (32-row tile, 64-element chunk, MFMA
+// step, half, row in tile, element), so that element (n, k) sits at
+//   ((n/32) (K/64) + k/64) 2048 + (k%64)/16 512 + ((k%16)/8 32 + n%32) 8 + k%8
+// and each operand load of a wave reads 1 KiB of contiguous memory.
+__device__ __forceinline__ int64_t packed_offset(int64_t n, int64_t k, int64_t K) {
+  return ((n >> 5) * (K >> 6) + (k >> 6)) * 2048 + ((k >> 4) & 3) * 512 + ((((k >> 3) & 1) << 5) + (n & 31)) * 8 +
+         (k & 7);
+}
 
 // ------------------------------------------------------------------ strided VALU GEMM
 struct GemmView {
   int64_t g, f, k;  // element strides: batch, free index, contraction index
+};
+
+// Packed addressing of an operand: its (n, k) in the packed weight are
+// n = g ng + f nf + k nk and k = g kg + f kf + k kk (f the free index, k the
+// contraction index of the operand, or for C the index j), K the packed
+// weight's contraction length.
+struct PackMap {
+  int64_t ng, nf, nk, kg, kf, kk, K;
 };
 
 // C[g](i, j) = sum_k A[g](i, k) B[g](k, j) with
@@ -53,16 +75,16 @@ constexpr int kT = 64;   // output tile edge
 constexpr int kKT = 16;  // contraction depth per LDS stage
 constexpr int kThreads = 256;
 
-template <typename TA, typename TB, typename TC>
+template <typename TA, typename TB, typename TC, bool PB, bool PC>
 __global__ __launch_bounds__(kThreads) void gemm_strided(const TA* __restrict__ A, GemmView a,
                                                           const TB* __restrict__ Bm, GemmView b, TC* __restrict__ C,
-                                                          GemmView c, int M, int N, int K) {
+                                                          GemmView c, PackMap pb, PackMap pc, int M, int N, int K) {
   __shared__ __align__(16) float As[kKT][kT];  // As[k][i]
   __shared__ __align__(16) float Bs[kKT][kT];  // Bs[k][j]
   const int64_t g = blockIdx.z;
   const int i0 = blockIdx.y * kT, j0 = blockIdx.x * kT, tid = threadIdx.x;
   const TA* Ag = A + g * a.g;
-  const TB* Bg = Bm + g * b.g;
+  const TB* Bg = Bm + (PB ? 0 : g * b.g);
   const int ti = 4 * (tid >> 4), tj = 4 * (tid & 15);  // this thread's rows ti..ti+3, columns tj..tj+3
   // tile loads: element e = tid + 256 q of the 16 x 64 stage, the unit-stride
   // axis fastest so that neighbouring threads read neighbouring elements
@@ -76,7 +98,12 @@ __global__ __launch_bounds__(kThreads) void gemm_strided(const TA* __restrict__ 
       const int bk = b_kfast ? (e & 15) : (e >> 6), bj = b_kfast ? (e >> 4) : (e & 63);
       const int gai = i0 + ai, gak = k0 + ak, gbj = j0 + bj, gbk = k0 + bk;
       As[ak][ai] = (gai < M && gak < K) ? Storage<TA>::load(Ag + gai * a.f + gak * a.k) : 0.f;
-      Bs[bk][bj] = (gbj < N && gbk < K) ? Storage<TB>::load(Bg + gbj * b.f + gbk * b.k) : 0.f;
+      int64_t bo;
+      if constexpr (PB)
+        bo = packed_offset(g * pb.ng + gbj * pb.nf + gbk * pb.nk, g * pb.kg + gbj * pb.kf + gbk * pb.kk, pb.K);
+      else
+        bo = gbj * b.f + gbk * b.k;
+      Bs[bk][bj] = (gbj < N && gbk < K) ? Storage<TB>::load(Bg + bo) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -91,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void gemm_strided(const TA* __restrict__ 
     }
     __syncthreads();
   }
-  TC* Cg = C + g * c.g;
+  TC* Cg = C + (PC ? 0 : g * c.g);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = i0 + ti + u;
@@ -99,7 +126,13 @@ __global__ __launch_bounds__(kThreads) void gemm_strided(const TA* __restrict__ 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int j = j0 + tj + v;
-      if (j < N) Storage<TC>::store(Cg + i * c.f + j * c.k, acc[u][v]);
+      if (j >= N) continue;
+      int64_t co;
+      if constexpr (PC)
+        co = packed_offset(g * pc.ng + i * pc.nf + j * pc.nk, g * pc.kg + i * pc.kf + j * pc.kk, pc.K);
+      else
+        co = i * c.f + j * c.k;
+      Storage<TC>::store(Cg + co, acc[u][v]);
     }
   }
 }
@@ -136,18 +169,26 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
                     (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16));
 }
 
-// hi + lo split of eight floats into two 16-byte groups of bf16
+// Two floats to a pair of bf16 (low half: a), by the hardware conversion
+// (round to nearest even).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2 w = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf16x2));
+}
+
+// hi + lo split of eight floats into two 16-byte groups of bf16:
+// hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ void split_hilo(const uint4& p, const uint4& q, uint4& hi, uint4& lo) {
-  const float x[8] = {__uint_as_float(p.x), __uint_as_float(p.y), __uint_as_float(p.z), __uint_as_float(p.w),
-                      __uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w)};
-  uint32_t h[8], l[8];
+  const uint32_t in[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    h[e] = f32_to_bf16_bits(x[e]);
-    l[e] = f32_to_bf16_bits(x[e] - bf16_bits_to_f32((uint16_t)h[e]));
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = __uint_as_float(in[2 * e]), x1 = __uint_as_float(in[2 * e + 1]);
+    h[e] = pk_bf16(x0, x1);
+    l[e] = pk_bf16(x0 - __uint_as_float(h[e] << 16), x1 - __uint_as_float(h[e] & 0xffff0000u));
   }
-  hi = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16);
-  lo = make_uint4(l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // Columns per workgroup: four waves, each owning CT 32-column MFMA tiles.
@@ -205,9 +246,11 @@ __global__ __launch_bounds__(kThreads) void linear_mfma(const void* __restrict__
   const int c_lo = ky * per, c_hi = min(nch, c_lo + per);
   const int nw = n0 + wave * 32 * CT;  // this wave's first column
 
-  const uint16_t* wrow[CT];
+  // this wave's column tiles in the packed weight: chunk c of tile u starts
+  // at wtile[u] + 2048 c, step s of it 512 further per step, lane l at 8 l
+  const uint16_t* wtile[CT];
 #pragma unroll
-  for (int u = 0; u < CT; ++u) wrow[u] = W + (size_t)(nw + 32 * u + (lane & 31)) * K + 8 * hi;
+  for (int u = 0; u < CT; ++u) wtile[u] = W + (size_t)((nw >> 5) + u) * nch * 2048 + 8 * lane;
 
   // X staging: thread tid covers 8-element groups g = tid and tid + 256 of
   // the chunk (row g >> 3, group g & 7)
@@ -255,11 +298,11 @@ __global__ __launch_bounds__(kThreads) void linear_mfma(const void* __restrict__
     }
   };
   auto load_w = [&](int c, uint4(&w)[CT][4]) {
-    const size_t o = (size_t)c * kLChunk;
+    const size_t o = (size_t)c * 2048;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int u = 0; u < CT; ++u) w[u][s] = *reinterpret_cast<const uint4*>(wrow[u] + o + 16 * s);
+      for (int u = 0; u < CT; ++u) w[u][s] = *reinterpret_cast<const uint4*>(wtile[u] + o + 512 * s);
   };
 
   f32x16 acc[2][CT];
@@ -370,11 +413,12 @@ __global__ __launch_bounds__(kThreads) void linear_finalize(const float* __restr
       pack_bf16x4(s.x, s.y, s.z, s.w);
 }
 
-template <typename TA, typename TB, typename TC>
-hipError_t gemm(const TA* A, GemmView a, const TB* Bm, GemmView b, TC* C, GemmView c, int M, int N, int K, int batch,
-                hipStream_t stream) {
+template <bool PB, bool PC, typename TA, typename TB, typename TC>
+hipError_t gemm(const TA* A, GemmView a, const TB* Bm, GemmView b, TC* C, GemmView c, PackMap pb, PackMap pc, int M,
+                int N, int K, int batch, hipStream_t stream) {
   const dim3 grid((N + kT - 1) / kT, (M + kT - 1) / kT, batch);
-  hipLaunchKernelGGL((gemm_strided<TA, TB, TC>), grid, dim3(kThreads), 0, stream, A, a, Bm, b, C, c, M, N, K);
+  hipLaunchKernelGGL((gemm_strided<TA, TB, TC, PB, PC>), grid, dim3(kThreads), 0, stream, A, a, Bm, b, C, c, pb, pc,
+                     M, N, K);
   return hipGetLastError();
 }
 
@@ -416,36 +460,49 @@ bool fused_output_mfma_supported(const mla_dims& d, int d_out) {
 }
 
 hipError_t launch_fold_query(const mla_dims& d, int d_in, const void* w_in, const void* w_uk, void* w_fused,
-                             hipStream_t stream) {
-  // C[h](c, i) = sum_n w_uk[h, n, c] w_in[h, n, i]
+                             bool packed, hipStream_t stream) {
+  // C[h](c, i) = sum_n w_uk[h, n, c] w_in[h, n, i], stored at w_fused[h, c, i]
+  // (packed: row h d_c + c, column i of W~_Q viewed as [H d_c x d_in])
   const GemmView a{(int64_t)d.d_nope * d.d_c, 1, d.d_c};
   const GemmView b{(int64_t)d.d_nope * d_in, 1, d_in};
   const GemmView c{(int64_t)d.d_c * d_in, d_in, 1};
-  if (d.dtype == MLA_BF16)
-    return gemm(static_cast<const uint16_t*>(w_uk), a, static_cast<const uint16_t*>(w_in), b,
-                static_cast<uint16_t*>(w_fused), c, d.d_c, d_in, d.d_nope, d.num_heads, stream);
-  return gemm(static_cast<const float*>(w_uk), a, static_cast<const float*>(w_in), b, static_cast<float*>(w_fused), c,
-              d.d_c, d_in, d.d_nope, d.num_heads, stream);
+  const PackMap none{}, pc{d.d_c, 1, 0, 0, 0, 1, d_in};
+  const int M = d.d_c, N = d_in, K = d.d_nope, G = d.num_heads;
+  if (d.dtype == MLA_BF16) {
+    const auto* A = static_cast<const uint16_t*>(w_uk);
+    const auto* B = static_cast<const uint16_t*>(w_in);
+    auto* C = static_cast<uint16_t*>(w_fused);
+    return packed ? gemm<false, true>(A, a, B, b, C, c, none, pc, M, N, K, G, stream)
+                  : gemm<false, false>(A, a, B, b, C, c, none, none, M, N, K, G, stream);
+  }
+  return gemm<false, false>(static_cast<const float*>(w_uk), a, static_cast<const float*>(w_in), b,
+                            static_cast<float*>(w_fused), c, none, none, M, N, K, G, stream);
 }
 
 hipError_t launch_fold_output(const mla_dims& d, int d_out, const void* w_o, const void* w_uv, void* w_fused,
-                              hipStream_t stream) {
+                              bool packed, hipStream_t stream) {
   // C[h](r, c) = sum_v w_o[r, h d_v + v] w_uv[h, v, c], stored at w_fused[r, h d_c + c]
   const int64_t Hdv = (int64_t)d.num_heads * d.d_v, Hdc = (int64_t)d.num_heads * d.d_c;
   const GemmView a{d.d_v, Hdv, 1};
   const GemmView b{(int64_t)d.d_v * d.d_c, 1, d.d_c};
   const GemmView c{d.d_c, Hdc, 1};
-  if (d.dtype == MLA_BF16)
-    return gemm(static_cast<const uint16_t*>(w_o), a, static_cast<const uint16_t*>(w_uv), b,
-                static_cast<uint16_t*>(w_fused), c, d_out, d.d_c, d.d_v, d.num_heads, stream);
-  return gemm(static_cast<const float*>(w_o), a, static_cast<const float*>(w_uv), b, static_cast<float*>(w_fused), c,
-              d_out, d.d_c, d.d_v, d.num_heads, stream);
+  const PackMap none{}, pc{0, 1, 0, d.d_c, 0, 1, Hdc};
+  const int M = d_out, N = d.d_c, K = d.d_v, G = d.num_heads;
+  if (d.dtype == MLA_BF16) {
+    const auto* A = static_cast<const uint16_t*>(w_o);
+    const auto* B = static_cast<const uint16_t*>(w_uv);
+    auto* C = static_cast<uint16_t*>(w_fused);
+    return packed ? gemm<false, true>(A, a, B, b, C, c, none, pc, M, N, K, G, stream)
+                  : gemm<false, false>(A, a, B, b, C, c, none, none, M, N, K, G, stream);
+  }
+  return gemm<false, false>(static_cast<const float*>(w_o), a, static_cast<const float*>(w_uv), b,
+                            static_cast<float*>(w_fused), c, none, none, M, N, K, G, stream);
 }
 
 hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* x, const void* q_rope,
-                              const void* w_fused, void* q_cat, bool mfma, hipStream_t stream) {
+                              const void* w_fused, void* q_cat, bool mfma, bool packed, hipStream_t stream) {
   const int M = d.batch * d.q_len, D = d.d_c + d.d_rope;
-  if (mfma) {
+  if (mfma) {  // the matrix-core path always reads the packed order
     const int N = d.num_heads * d.d_c;
     int per = 0;
     const int ks = linear_ksplit(M, N, d_in, linear_block<kQueryCT>(), 2, cus, 1, &per);
@@ -460,17 +517,21 @@ hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* 
   const GemmView a{0, d_in, 1};
   const GemmView b{(int64_t)d.d_c * d_in, d_in, 1};
   const GemmView c{D, (int64_t)d.num_heads * D, 1};
-  hipError_t e;
+  const PackMap none{}, pb{d.d_c, 1, 0, 0, 0, 1, d_in};
   const int64_t rows = (int64_t)M * d.num_heads;
+  hipError_t e;
   if (d.dtype == MLA_BF16) {
-    e = gemm(static_cast<const uint16_t*>(x), a, static_cast<const uint16_t*>(w_fused), b,
-             static_cast<uint16_t*>(q_cat), c, M, d.d_c, d_in, d.num_heads, stream);
+    const auto* A = static_cast<const uint16_t*>(x);
+    const auto* B = static_cast<const uint16_t*>(w_fused);
+    auto* C = static_cast<uint16_t*>(q_cat);
+    e = packed ? gemm<true, false>(A, a, B, b, C, c, pb, none, M, d.d_c, d_in, d.num_heads, stream)
+               : gemm<false, false>(A, a, B, b, C, c, none, none, M, d.d_c, d_in, d.num_heads, stream);
     if (e == hipSuccess && d.d_rope > 0)
       hipLaunchKernelGGL(pass_rope<uint16_t>, dim3(256), dim3(kThreads), 0, stream,
-                         static_cast<const uint16_t*>(q_rope), static_cast<uint16_t*>(q_cat), rows, d.d_c, d.d_rope);
+                         static_cast<const uint16_t*>(q_rope), C, rows, d.d_c, d.d_rope);
   } else {
-    e = gemm(static_cast<const float*>(x), a, static_cast<const float*>(w_fused), b, static_cast<float*>(q_cat), c, M,
-             d.d_c, d_in, d.num_heads, stream);
+    e = gemm<false, false>(static_cast<const float*>(x), a, static_cast<const float*>(w_fused), b,
+                           static_cast<float*>(q_cat), c, none, none, M, d.d_c, d_in, d.num_heads, stream);
     if (e == hipSuccess && d.d_rope > 0)
       hipLaunchKernelGGL(pass_rope<float>, dim3(256), dim3(kThreads), 0, stream, static_cast<const float*>(q_rope),
                          static_cast<float*>(q_cat), rows, d.d_c, d.d_rope);
@@ -479,9 +540,9 @@ hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* 
 }
 
 hipError_t launch_fused_output(const mla_dims& d, int d_out, int cus, const float* o, const void* w_fused, void* y,
-                               float* ws, bool mfma, hipStream_t stream) {
+                               float* ws, bool mfma, bool packed, hipStream_t stream) {
   const int M = d.batch * d.q_len, K = d.num_heads * d.d_c;
-  if (mfma) {
+  if (mfma) {  // the matrix-core path always reads the packed order
     int per = 0;
     const int ks = linear_ksplit(M, d_out, K, linear_block<kOutputCT>(), kOutputSlots, cus, kLMaxKSplit, &per);
     const LinearOut out{static_cast<uint16_t*>(y), d_out, d_out, 0, nullptr, 0, 1};
@@ -498,9 +559,15 @@ hipError_t launch_fused_output(const mla_dims& d, int d_out, int cus, const floa
   const GemmView a{0, K, 1};
   const GemmView b{0, K, 1};
   const GemmView c{0, d_out, 1};
-  if (d.dtype == MLA_BF16)
-    return gemm(o, a, static_cast<const uint16_t*>(w_fused), b, static_cast<uint16_t*>(y), c, M, d_out, K, 1, stream);
-  return gemm(o, a, static_cast<const float*>(w_fused), b, static_cast<float*>(y), c, M, d_out, K, 1, stream);
+  const PackMap none{}, pb{0, 1, 0, 0, 0, 1, K};
+  if (d.dtype == MLA_BF16) {
+    const auto* B = static_cast<const uint16_t*>(w_fused);
+    auto* C = static_cast<uint16_t*>(y);
+    return packed ? gemm<true, false>(o, a, B, b, C, c, pb, none, M, d_out, K, 1, stream)
+                  : gemm<false, false>(o, a, B, b, C, c, none, none, M, d_out, K, 1, stream);
+  }
+  return gemm<false, false>(o, a, static_cast<const float*>(w_fused), b, static_cast<float*>(y), c, none, none, M,
+                            d_out, K, 1, stream);
 }
 
 }  // namespace mla

@@ -69,20 +69,21 @@ hipError_t launch_prefill(const mla_dims& d, int tokens, int max_seqlen, const i
                           const void* w_uv, float scale, int causal, void* out, float* lse, void* ws, bool mfma,
                           hipStream_t stream);
 
-// offline weight folds and the fused runtime products (fold.hip): matrix-core
-// runtime path for bf16 with the support tests below, portable VALU path
-// otherwise; folds always take the portable batched GEMM
-hipError_t launch_fold_query(const mla_dims& d, int d_in, const void* w_in, const void* w_uk, void* w_fused,
-                             hipStream_t stream);
-hipError_t launch_fold_output(const mla_dims& d, int d_out, const void* w_o, const void* w_uv, void* w_fused,
-                              hipStream_t stream);
+// offline weight folds and the fused runtime products (fold.hip).  The
+// support tests say where the matrix-core path serves a shape; there the
+// fused weights are stored in the packed fragment order (packed = true),
+// which the folds write and both kernel families of the products read.
 bool fused_query_mfma_supported(const mla_dims& d, int d_in);
 bool fused_output_mfma_supported(const mla_dims& d, int d_out);
+hipError_t launch_fold_query(const mla_dims& d, int d_in, const void* w_in, const void* w_uk, void* w_fused,
+                             bool packed, hipStream_t stream);
+hipError_t launch_fold_output(const mla_dims& d, int d_out, const void* w_o, const void* w_uv, void* w_fused,
+                              bool packed, hipStream_t stream);
 int linear_max_ksplit();
 int linear_ksplit(int M, int N, int K, int block, int slots, int cus, int max_ks, int* per_out);
 hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* x, const void* q_rope,
-                              const void* w_fused, void* q_cat, bool mfma, hipStream_t stream);
+                              const void* w_fused, void* q_cat, bool mfma, bool packed, hipStream_t stream);
 hipError_t launch_fused_output(const mla_dims& d, int d_out, int cus, const float* o, const void* w_fused, void* y,
-                               float* ws, bool mfma, hipStream_t stream);
+                               float* ws, bool mfma, bool packed, hipStream_t stream);
 
 }  // namespace mla

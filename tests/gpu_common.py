@@ -52,6 +52,19 @@ def assert_parity(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
         assert rel <= BF16_REL_L2, f"{what}: rel_l2 {rel:.3e} > {BF16_REL_L2}"
 
 
+def pack_fused_weight(w: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """The fragment order the header defines for a fused weight viewed as [n x k]: element (r, c) moves to
+    ((r/32)(k/64) + c/64) 2048 + ((c%64)/16) 512 + (((c%16)/8) 32 + r%32) 8 + c%8 (a pure reordering)."""
+    return (w.reshape(n // 32, 32, k // 64, 4, 2, 8).permute(0, 2, 3, 4, 1, 5).contiguous()
+            .reshape(w.shape))
+
+
+def unpack_fused_weight(w: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """Inverse of pack_fused_weight."""
+    return (w.reshape(n // 32, k // 64, 4, 2, 32, 8).permute(0, 4, 1, 2, 3, 5).contiguous()
+            .reshape(w.shape))
+
+
 PLAN_TILE = 64
 
 

@@ -275,3 +275,17 @@ def test_fused_output_invalid_args(over):
     args.update(over)
     assert _call("mla_fused_output", ctypes.byref(bf), args["d_out"], args["o"], args["w"], args["y"], args["ws"],
                  args["ws_bytes"], None) == -1
+
+
+def test_fused_weight_packed_predicates():
+    bf = _dims(dtype=libmla.MLA_BF16, batch=64, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128,
+               block_size=64)
+    assert libmla.mla_fused_query_weight_packed(bf, 1536)
+    assert not libmla.mla_fused_query_weight_packed(bf, 1536 + 32)  # d_in not a multiple of 64
+    assert libmla.mla_fused_output_weight_packed(bf, 7168)
+    assert not libmla.mla_fused_output_weight_packed(bf, 7168 + 64)  # d_out not a multiple of 256
+    assert not libmla.mla_fused_query_weight_packed(_dims(), 128)  # float32 storage: row-major
+    assert not libmla.mla_fused_output_weight_packed(_dims(), 256)
+    for bad in (0, -5, 1 << 17):
+        assert not libmla.mla_fused_query_weight_packed(bf, bad)
+        assert not libmla.mla_fused_output_weight_packed(bf, bad)
