@@ -6,7 +6,9 @@ split-KV attention, then the log-sum-exp combine and absorb_out (one fused
 call), for every sequence of the workload.  Inputs are seeded synthetic
 tensors already resident in HBM.  The same line also reports, measured on
 their own: the cache append of the step's new tokens and the prefill of a
-4 x 4096-token batch (--no-prefill skips it).
+4 x 4096-token batch (--no-prefill skips it), the step over the workload's
+FP8-cache twin (--no-fp8), and the offline weight folds with the fused
+products that replace absorb_q and absorb_out (--no-folds).
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-prefill]
@@ -146,6 +148,95 @@ def cpu_baseline(prob, budget_s=15.0, max_s=30.0):
     }
 
 
+FOLD_D_IN = 1536  # query latent width: the input of the fused query weight
+
+
+def measure_folds(prob, r, stream, K, warmup):
+    """The offline folds and the fused products, with the unfolded route beside them.
+
+    Fused query: q_cat = [W~_Q x ; q^R] replaces (W_in x, then absorb_q).
+    Fused output: y = W~^O o replaces (absorb_out, then W^O u).  The unfolded
+    route's plain projections W_in x and W^O u are not libmla calls: they run
+    as torch.matmul (hipBLASLt) here, for comparison only.  Algorithmic bytes
+    of a fused product: its weight, its inputs and its output once.
+    """
+    import torch
+
+    from mla_latent_kv_14_amd import binding as libmla
+    from mla_latent_kv_14_amd.inputs import make_fold_inputs
+
+    wl = prob.wl
+    dev = "cuda:0"
+    fi = make_fold_inputs(prob, d_in=FOLD_D_IN)
+    d = r.dims
+    M, H, D = wl.batch * wl.q_len, wl.heads, wl.d_c + wl.d_rope
+    x, w_in, w_o, o = (t.to(dev) for t in (fi.x, fi.w_in, fi.w_o, fi.o))
+    w_uk, w_uv, q_rope = (t.to(dev) for t in (prob.w_uk, prob.w_uv, prob.q_rope))
+    dt = w_in.dtype
+    wq = torch.empty((H, wl.d_c, fi.d_in), dtype=dt, device=dev)
+    wo = torch.empty((fi.d_out, H * wl.d_c), dtype=dt, device=dev)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    fold_q = lambda: libmla.mla_fold_query_weight(d, fi.d_in, w_in, w_uk, wq)
+    fold_o = lambda: libmla.mla_fold_output_weight(d, fi.d_out, w_o, w_uv, wo)
+    fold_q()
+    fold_o()
+    fold_q_us, fold_o_us = timed(fold_q, 2), timed(fold_o, 2)
+
+    q_cat = torch.empty((wl.batch, wl.q_len, H, D), dtype=dt, device=dev)
+    ws = torch.empty((max(libmla.mla_fused_output_workspace_bytes(d, fi.d_out), 4) // 4,), dtype=torch.float32,
+                     device=dev)
+    y = torch.empty((wl.batch, wl.q_len, fi.d_out), dtype=dt, device=dev)
+    fq = lambda: libmla.mla_fused_query(d, fi.d_in, x, q_rope, wq, q_cat)
+    fo = lambda: libmla.mla_fused_output(d, fi.d_out, o, wo, y, ws)
+    q_nope = torch.empty((M, H * wl.d_nope), dtype=dt, device=dev)
+    u = torch.empty((wl.batch, wl.q_len, H, wl.d_v), dtype=dt, device=dev)
+    y2 = torch.empty((M, fi.d_out), dtype=dt, device=dev)
+    w_uq = w_in.reshape(H * wl.d_nope, fi.d_in)
+
+    def unfolded_q():
+        torch.matmul(x.reshape(M, fi.d_in), w_uq.t(), out=q_nope)
+        libmla.mla_absorb_q(d, q_nope.view(wl.batch, wl.q_len, H, wl.d_nope), q_rope, w_uk, q_cat)
+
+    def unfolded_o():
+        libmla.mla_absorb_out(d, o, w_uv, u)
+        torch.matmul(u.view(M, H * wl.d_v), w_o.t(), out=y2)
+
+    for fn in (fq, fo, unfolded_q, unfolded_o):
+        for _ in range(warmup):
+            fn()
+    fq_us, fo_us = timed(fq, K), timed(fo, K)
+    uq_us, uo_us = timed(unfolded_q, K), timed(unfolded_o, K)
+    esz = 2 if dt == torch.bfloat16 else 4
+    q_bytes = wq.numel() * esz + x.numel() * esz + q_rope.numel() * esz + q_cat.numel() * esz
+    o_bytes = wo.numel() * esz + o.numel() * 4 + y.numel() * esz
+    res = {
+        "d_in": fi.d_in, "d_out": fi.d_out,
+        "fold_query_ms": fold_q_us / 1e3, "fold_output_ms": fold_o_us / 1e3,
+        "fused_query": {"us": fq_us, "alg_bytes": q_bytes, "gbs": q_bytes / (fq_us * 1e-6) / 1e9,
+                        "hbm_frac": q_bytes / (fq_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                        "weight_bytes": wq.numel() * esz},
+        "fused_output": {"us": fo_us, "alg_bytes": o_bytes, "gbs": o_bytes / (fo_us * 1e-6) / 1e9,
+                         "hbm_frac": o_bytes / (fo_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "weight_bytes": wo.numel() * esz},
+        "unfolded_query_us": uq_us, "unfolded_output_us": uo_us,
+        "unfolded_note": "W_in x and W^O u by torch.matmul (hipBLASLt), absorb_q / absorb_out by libmla",
+    }
+    log(f"bench: folds: fused query {fq_us:.1f} us ({res['fused_query']['gbs']:.0f} GB/s) vs unfolded {uq_us:.1f} us;"
+        f" fused output {fo_us:.1f} us ({res['fused_output']['gbs']:.0f} GB/s) vs unfolded {uo_us:.1f} us;"
+        f" folds {fold_q_us / 1e3:.2f} + {fold_o_us / 1e3:.2f} ms offline")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +248,7 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time HIP-graph replays instead of eager launches")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache twin of the workload")
+    ap.add_argument("--no-folds", action="store_true", help="skip the weight folds and fused products")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -166,7 +258,8 @@ def main():
 
     import torch
 
-    from mla_latent_kv_14_amd.inputs import WORKLOADS, make_append_inputs, make_prefill_problem, make_problem, workload
+    from mla_latent_kv_14_amd.inputs import (WORKLOADS, make_append_inputs, make_fold_inputs, make_prefill_problem,
+                                             make_problem, workload)
     from mla_latent_kv_14_amd.runner import DecodeRunner, PrefillRunner
 
     if not torch.cuda.is_available():
@@ -318,6 +411,10 @@ def main():
         log(f"bench: FP8 cache ({twin}): {f_step * 1e3:.1f} us/step, attention {f_kernel_us:.1f} us")
         del fr
 
+    folds = None
+    if not args.no_folds:
+        folds = measure_folds(prob, r, stream, K, args.warmup)
+
     alg_bytes, flops = algorithmic_work(prob)
     dec_s = decode_kernel_us * 1e-6
     achieved_gbs = alg_bytes / dec_s / 1e9
@@ -359,6 +456,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill": prefill,
         "fp8_cache": fp8,
+        "weight_folds": folds,
         "cache_append": {"us_per_call": append_us, "d_model": app.d_model, "alg_bytes": ap_bytes,
                          "gbs": ap_bytes / (append_us * 1e-6) / 1e9,
                          "hbm_frac": ap_bytes / (append_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
