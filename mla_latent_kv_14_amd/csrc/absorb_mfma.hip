@@ -31,7 +31,8 @@ constexpr int kNQ = 128;   // absorb_q: columns of q~ per workgroup
 // ------------------------------------------------------------------ absorb_q
 // grid (H, d_c / 128, ceil(M / 64)): workgroup (h, nq, mt) computes columns
 // 128 nq .. 128 nq + 127 of q~ for rows 64 mt .. 64 mt + 63; wave w takes the
-// 32 columns 32 w .. 32 w + 31 of that quarter.  The MFMA computes q~^T =
+// 32 columns 32 w .. 32 w + 31 of that quarter.  The W quarter and the 64
+// q_nope rows are both staged in LDS once per workgroup.  The MFMA computes q~^T =
 // W_UK[h]^T . q_nope^T (A = W_UK^T from the LDS transpose read, B = q_nope
 // rows), so each lane ends up with four consecutive latent columns of one row
 // and stores them as one 8-byte write.
@@ -47,17 +48,16 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const int D = kDC + d_r;
 
-  // every q_nope operand of the workgroup's rows is requested first: both
-  // 32-row tiles, 8 x 16 B per lane each (rows past M read row M - 1)
-  uint4 a[2][kDN / 16];
+  // the workgroup's q_nope rows (64 x 256 B) are staged once in LDS, row m's
+  // chunk c at slot c ^ (m & 15); rows past M read row M - 1
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kRowsQ * kDN * 2];
+  uint4 qv[(kRowsQ * kDN / 8) / kThreads];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int m = min(mbase + 32 * t + (lane & 31), M - 1);
-    const uint16_t* src = q_nope + ((size_t)m * H + h) * kDN + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < kDN / 16; ++ks) a[t][ks] = *reinterpret_cast<const uint4*>(src + 16 * ks);
+  for (int i = 0; i < (kRowsQ * kDN / 8) / kThreads; ++i) {
+    const int q = i * kThreads + tid, r = q >> 4, c = q & 15;
+    const int m = min(mbase + r, M - 1);
+    qv[i] = *reinterpret_cast<const uint4*>(q_nope + ((size_t)m * H + h) * kDN + 8 * c);
   }
-
   const uint16_t* w = w_uk + (size_t)h * kDN * kDC + nq * kNQ;
   uint4 wv[(kDN * kNQ / 8) / kThreads];
 #pragma unroll
@@ -83,7 +83,20 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
     const int k = q >> 4, c = q & 15;
     *reinterpret_cast<uint4*>(wt + k * 256 + ((c ^ (4 * (k & 3))) * 16)) = wv[i];
   }
+#pragma unroll
+  for (int i = 0; i < (kRowsQ * kDN / 8) / kThreads; ++i) {
+    const int q = i * kThreads + tid, r = q >> 4, c = q & 15;
+    *reinterpret_cast<uint4*>(qs + r * 256 + ((c ^ (r & 15)) * 16)) = qv[i];
+  }
   __syncthreads();
+  uint4 a[2][kDN / 16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = 32 * t + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < kDN / 16; ++ks)
+      a[t][ks] = *reinterpret_cast<const uint4*>(qs + r * 256 + (((2 * ks + hi) ^ (r & 15)) * 16));
+  }
 
   // transpose-read supplier mapping (see the decode kernel): lane supplies row
   // 16 ks + 8 (g16 >> 1) + 4 h + (j16 >> 2), columns 32 w + 16 (g16 & 1) + 4 (j16 & 3)
