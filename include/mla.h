@@ -346,7 +346,8 @@ int mla_fold_query_weight(const mla_dims* dims, int32_t d_in, const void* w_in, 
  * [H,d_c,d_in] in the fused weight storage order, q_cat [B,Lq,H,d_c+d_rope],
  * all in the storage type.  Float32 accumulation, one rounding.  Where the
  * weight is in fragment order the product runs on the matrix cores; other
- * supported shapes run on a portable kernel. */
+ * supported shapes run on a portable kernel.  MLA_ERR_UNSUPPORTED when
+ * B*Lq > 4194240. */
 int mla_fused_query(const mla_dims* dims, int32_t d_in, const void* x, const void* q_rope, const void* w_fused,
                     void* q_cat, void* stream);
 
@@ -378,7 +379,8 @@ int mla_fused_output_workspace_bytes(const mla_dims* dims, int32_t d_out, size_t
  * Float32 accumulation; on the matrix cores (where the weight is in fragment
  * order) o_latent enters as a bf16 hi + lo pair and the split of H*d_c, and
  * so the order of the float32 additions, follows the device's compute-unit
- * count: reproducible on one device type. */
+ * count: reproducible on one device type.  MLA_ERR_UNSUPPORTED when B*Lq >
+ * 4194240. */
 int mla_fused_output(const mla_dims* dims, int32_t d_out, const float* o_latent, const void* w_fused, void* y,
                      void* workspace, size_t workspace_bytes, void* stream);
 

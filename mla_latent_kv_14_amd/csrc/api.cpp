@@ -19,6 +19,9 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxBatch = 1 << 20;
 constexpr int kMaxDModel = 1 << 16;
+// rows (B * q_len) of the fused products: the portable kernel's row blocks
+// of 64 must fit a grid dimension
+constexpr int64_t kMaxFusedRows = (int64_t)65535 * 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
@@ -451,6 +454,7 @@ int mla_fused_query(const mla_dims* d, int32_t d_in, const void* x, const void* 
   if (d_in < 1 || d_in > kMaxDModel) return MLA_ERR_INVALID_ARG;
   if (!ptr_ok(x) || !ptr_ok(w_fused) || !ptr_ok(q_cat) || (d->d_rope > 0 && !ptr_ok(q_rope)))
     return MLA_ERR_INVALID_ARG;
+  if ((int64_t)d->batch * d->q_len > kMaxFusedRows) return MLA_ERR_UNSUPPORTED;
   const bool packed = mla::fused_query_mfma_supported(*d, d_in);
   const bool mfma = packed && !force_generic();
   int cus = 1;
@@ -486,6 +490,7 @@ int mla_fused_output(const mla_dims* d, int32_t d_out, const float* o_latent, co
   if (st != MLA_OK) return st;
   if (d_out < 1 || d_out > kMaxDModel) return MLA_ERR_INVALID_ARG;
   if (!ptr_ok(o_latent) || !ptr_ok(w_fused) || !ptr_ok(y)) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)d->batch * d->q_len > kMaxFusedRows) return MLA_ERR_UNSUPPORTED;
   size_t need = 0;
   mla_fused_output_workspace_bytes(d, d_out, &need);
   if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need)) return MLA_ERR_INVALID_ARG;

@@ -508,8 +508,9 @@ hipError_t launch_fused_query(const mla_dims& d, int d_in, int cus, const void* 
     const int ks = linear_ksplit(M, N, d_in, linear_block<kQueryCT>(), 2, cus, 1, &per);
     const LinearOut out{static_cast<uint16_t*>(q_cat), (int64_t)d.num_heads * D, d.d_c, D,
                         d.d_rope > 0 ? static_cast<const uint16_t*>(q_rope) : nullptr, d.d_rope, d.num_heads};
-    const int blocks = (N / linear_block<kQueryCT>()) * ((M + kLRows - 1) / kLRows) * ks;
-    hipLaunchKernelGGL((linear_mfma<false, kQueryCT, kQueryRing>), dim3(blocks), dim3(kThreads), 0, stream, x,
+    const int64_t blocks = (int64_t)(N / linear_block<kQueryCT>()) * ((M + kLRows - 1) / kLRows) * ks;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((linear_mfma<false, kQueryCT, kQueryRing>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, x,
                        static_cast<const uint16_t*>(w_fused), nullptr, out, M, N, d_in, per, ks);
     return hipGetLastError();
   }
@@ -546,8 +547,9 @@ hipError_t launch_fused_output(const mla_dims& d, int d_out, int cus, const floa
     int per = 0;
     const int ks = linear_ksplit(M, d_out, K, linear_block<kOutputCT>(), kOutputSlots, cus, kLMaxKSplit, &per);
     const LinearOut out{static_cast<uint16_t*>(y), d_out, d_out, 0, nullptr, 0, 1};
-    const int blocks = (d_out / linear_block<kOutputCT>()) * ((M + kLRows - 1) / kLRows) * ks;
-    hipLaunchKernelGGL((linear_mfma<true, kOutputCT, kOutputRing>), dim3(blocks), dim3(kThreads), 0, stream, o,
+    const int64_t blocks = (int64_t)(d_out / linear_block<kOutputCT>()) * ((M + kLRows - 1) / kLRows) * ks;
+    if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((linear_mfma<true, kOutputCT, kOutputRing>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, o,
                        static_cast<const uint16_t*>(w_fused), ws, out, M, d_out, K, per, ks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ks == 1) return e;

@@ -289,3 +289,11 @@ def test_fused_weight_packed_predicates():
     for bad in (0, -5, 1 << 17):
         assert not libmla.mla_fused_query_weight_packed(bf, bad)
         assert not libmla.mla_fused_output_weight_packed(bf, bad)
+
+
+def test_fused_products_row_limit():
+    big = _dims(batch=1 << 20, q_len=8)  # 8M rows: past the fused products' limit
+    assert _call("mla_fused_query", ctypes.byref(big), 96, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == \
+        libmla.MLA_ERR_UNSUPPORTED
+    assert _call("mla_fused_output", ctypes.byref(big), 64, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1 << 40, None) == \
+        libmla.MLA_ERR_UNSUPPORTED
