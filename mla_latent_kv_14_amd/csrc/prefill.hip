@@ -17,7 +17,8 @@
 //   upproject_mfma  Kn = c_kv . W_UK^T and V = c_kv . W_UV^T as NT GEMMs
 //                   (T x 512 times 512 x 128 H), 128 x 128 output tiles, both
 //                   operands staged in LDS by the LDS-DMA path, 2 x 2 MFMA
-//                   tiles per wave; it also copies k^R into R.
+//                   tiles per wave, the output tile written out through LDS
+//                   in 256-B row segments; it also copies k^R into R.
 //   attn_mfma       one workgroup per (sequence, head, 256-query block),
 //                   eight waves of 32 queries.  32-key tiles [Kn | V | k^R]
 //                   (640 B per key) go HBM -> LDS once per workgroup in a
@@ -143,21 +144,32 @@ __global__ __launch_bounds__(kGThreads, 2) void upproject_mfma(const uint16_t* _
     }
   }
 
-  // lane (m = lane & 31, hi): element r of acc[tn][tm] is column
-  // 8 (r >> 2) + 4 hi + (r & 3) of the 32-column tile tn
+  // the output tile goes through LDS so that every store writes 16 B of a
+  // 256-B row segment: lane (m = lane & 31, hi) holds, in acc[tn][tm],
+  // columns 8 (r >> 2) + 4 hi + (r & 3) of the 32-column tile tn
+  block_sync();  // every wave is done with the operand stages
+  uint8_t* ot = smem;  // [128 rows][256 B], 16-B chunk c of row r at c ^ (r & 15)
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm) {
-    const int m = m0 + 64 * mh + 32 * tm + r32;
-    if (m >= M) continue;
+    const int r = 64 * mh + 32 * tm + r32;
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn) {
-      uint16_t* dst = dmat + (size_t)m * N + n0 + 64 * nh + 32 * tn + 4 * hi;
+    for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<uint2*>(dst + 8 * g) =
+      for (int g = 0; g < 4; ++g) {
+        const int col = 64 * nh + 32 * tn + 8 * g + 4 * hi;  // 4 columns = 8 B
+        const int c = col >> 3, half = (col >> 2) & 1;
+        *reinterpret_cast<uint2*>(ot + r * 256 + ((c ^ (r & 15)) << 4) + 8 * half) =
             make_uint2(pack_bf16(acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1]),
                        pack_bf16(acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3]));
-    }
+      }
+  }
+  block_sync();
+#pragma unroll
+  for (int i = 0; i < (kGT * 16) / kGThreads; ++i) {  // 8 chunks of 16 B per thread
+    const int q = i * kGThreads + tid, r = q >> 4, c = q & 15, m = m0 + r;
+    if (m < M)
+      *reinterpret_cast<uint4*>(dmat + (size_t)m * N + n0 + 8 * c) =
+          *reinterpret_cast<const uint4*>(ot + r * 256 + ((c ^ (r & 15)) << 4));
   }
 }
 
