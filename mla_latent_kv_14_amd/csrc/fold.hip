@@ -24,8 +24,9 @@
 // bound by streaming W from HBM.  Workgroup (column block, row block,
 // k-split) owns 128 (query) or 256 (output) columns and 64 rows over its
 // share of K; its four waves own disjoint columns.  X passes through LDS once
-// per workgroup, W goes straight from memory into the MFMA operands through a
-// three-chunk register ring.  A float32 X (the latent attention output) enters
+// per workgroup; W, stored in MFMA fragment order (below), goes straight from
+// memory into the MFMA operands through a register ring of three (query) or
+// four (output) chunks.  A float32 X (the latent attention output) enters
 // the bf16 MFMAs as hi + lo with hi, lo in bf16, so its rounding error is that
 // of about 16 mantissa bits.  With one split the workgroup writes the bf16
 // result; with several it writes a float32 partial, and a second kernel adds
