@@ -57,6 +57,7 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, misaligned pointer, bad split count */
   MLA_ERR_UNSUPPORTED = -2, /* valid but not implemented: dtype, widths or q_len outside the supported set */
+  MLA_ERR_WORKSPACE = -3,   /* the workspace is smaller than the matching *_workspace_bytes() call says */
   MLA_ERR_HIP = -4          /* the HIP runtime reported an error (launch or device query) */
 } mla_status;
 
@@ -94,8 +95,25 @@ int mla_absorb_q(const mla_dims* dims, const void* q_nope, const void* q_rope, c
  * shares the work evenly, given the longest sequence and the total token
  * count (host-side values the caller knows).  Result in [1, 4096].  Passing a
  * smaller S to mla_decode is allowed: the library then gives each workgroup a
- * longer token range and launches fewer of them. */
+ * longer token range and launches fewer of them.  MLA_ERR_INVALID_ARG when
+ * max_seq_len < 1, total_tokens < max_seq_len or num_splits is NULL. */
 int mla_decode_num_splits(const mla_dims* dims, int32_t max_seq_len, int64_t total_tokens,
+                          int32_t* num_splits);
+
+/* The same choice from the lengths themselves, for callers that hold them
+ * on the host.  seq_lens_host [B] int32 is a HOST array (read during the
+ * call, not retained) or NULL; with it, max_seq_len and the total are taken
+ * from the lengths (each clamped to [0, max_blocks_per_seq * block_size];
+ * max_seq_len is then ignored and may be 0).  With NULL every sequence is
+ * taken to be max_seq_len long (a batch of equal lengths; a batch of very
+ * unequal lengths is balanced better when its lengths are given).  The result
+ * equals mla_decode_num_splits(dims, max, total).  The _fp8 form sizes the
+ * FP8-cache decode (mla_decode_fp8).  MLA_ERR_INVALID_ARG when num_splits is
+ * NULL, or when seq_lens_host is NULL and max_seq_len < 1, or when every
+ * given length is 0. */
+int mla_choose_splits(const mla_dims* dims, const int32_t* seq_lens_host, int32_t max_seq_len,
+                      int32_t* num_splits);
+int mla_choose_splits_fp8(const mla_dims* dims, const int32_t* seq_lens_host, int32_t max_seq_len,
                           int32_t* num_splits);
 
 /* Bytes of device workspace mla_decode needs (the work schedule it computes
@@ -114,9 +132,10 @@ int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t*
  *   softmax_scale  multiplies every score (1/sqrt(d_nope + d_rope) for MLA);
  *               must be finite and > 0
  *   num_splits  S >= 1, the split dimension of the two outputs
- *   workspace   device scratch of at least mla_decode_workspace_bytes(),
- *               16-byte aligned; overwritten by every call, so calls sharing
- *               one workspace must be ordered on one stream
+ *   workspace   device scratch of at least mla_decode_workspace_bytes()
+ *               (MLA_ERR_WORKSPACE if workspace_bytes is smaller), 16-byte
+ *               aligned; overwritten by every call, so calls sharing one
+ *               workspace must be ordered on one stream
  *   o_partial   [B,Lq,H,S,d_c] float32: o_s = sum_{t in split} p_t c_t with p
  *               normalised within the split
  *   lse_partial [B,Lq,H,S] float32: natural-log log-sum-exp of the split's
@@ -237,7 +256,8 @@ int mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t d_model, size
  *   w_dkv   [d_c,d_model]   W^DKV (a Linear weight), storage type
  *   w_kr    [d_rope,d_model] W^KR, storage type (may be NULL if d_rope = 0)
  *   kv_cache [num_blocks,block_size,d_c+d_rope] storage type, updated in place
- *   workspace  at least mla_cache_append_workspace_bytes() bytes, contents
+ *   workspace  at least mla_cache_append_workspace_bytes() bytes
+ *              (MLA_ERR_WORKSPACE if workspace_bytes is smaller), contents
  *              on entry irrelevant (float32 split-K partials)
  * Products accumulate in float32; the RoPE angle, its sine and cosine and
  * the rotation are evaluated in float64; each value is rounded once to the
@@ -286,14 +306,18 @@ int mla_prefill_workspace_bytes(const mla_dims* dims, int32_t total_tokens, size
  *                                             (latent and rotated RoPE key)
  *   w_uk [H,d_nope,d_c], w_uv [H,d_v,d_c]     storage type
  *   out    [T,H,d_v] storage type;  lse [T,H] float32 (natural log), or NULL
- *   workspace  at least mla_prefill_workspace_bytes(); overwritten
+ *   workspace  at least mla_prefill_workspace_bytes() (MLA_ERR_WORKSPACE if
+ *              workspace_bytes is smaller); overwritten
  * Only dims->batch, num_heads, d_c, d_rope, d_nope, d_v and dtype are used
  * (the other fields must still be valid, e.g. 1).  Products accumulate in
  * float32; the up-projected K and V are rounded once to the storage type, and
  * for bf16 the softmax weights are rounded to bf16 before the weighted sum.
  * A sequence longer than max_seqlen or a cu_seqlens outside [0, T] is
  * undefined behaviour (reads stay inside the buffers).  MLA_ERR_UNSUPPORTED
- * when the bf16 workspace would reach 4 GiB (split the batch). */
+ * when the bf16 workspace would reach 4 GiB, or when the matrix-core
+ * attention grid (batch * num_heads * ceil(max_seqlen / 256) workgroups of
+ * 512 threads) would exceed 2^32 - 1 threads (split the batch); nothing is
+ * enqueued then. */
 int mla_prefill(const mla_dims* dims, int32_t total_tokens, int32_t max_seqlen, const int32_t* cu_seqlens,
                 const void* q_nope, const void* q_rope, const void* c_kv, const void* k_rope, const void* w_uk,
                 const void* w_uv, float softmax_scale, int32_t causal, void* out, float* lse, void* workspace,
@@ -375,7 +399,8 @@ int mla_fused_output_workspace_bytes(const mla_dims* dims, int32_t d_out, size_t
  * rounding.  o_latent [B,Lq,H,d_c] float32 (as mla_combine writes it),
  * w_fused [d_out, H*d_c] storage type in the fused weight storage order, y
  * [B,Lq,d_out] storage type; workspace at least
- * mla_fused_output_workspace_bytes() bytes, contents on entry irrelevant.
+ * mla_fused_output_workspace_bytes() bytes (MLA_ERR_WORKSPACE if
+ * workspace_bytes is smaller), contents on entry irrelevant.
  * Float32 accumulation; on the matrix cores (where the weight is in fragment
  * order) o_latent enters as a bf16 hi + lo pair and the split of H*d_c, and
  * so the order of the float32 additions, follows the device's compute-unit

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmla.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
 
-MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP = 0, -1, -2, -4
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = 0, -1, -2, -3, -4
 MLA_F32, MLA_BF16 = 0, 1
 
 
@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
     sig = {
         "mla_absorb_q": [D, P, P, P, P, P],
         "mla_decode_num_splits": [D, I32, I64, ctypes.POINTER(I32)],
+        "mla_choose_splits": [D, P, I32, ctypes.POINTER(I32)],
+        "mla_choose_splits_fp8": [D, P, I32, ctypes.POINTER(I32)],
         "mla_decode_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_decode": [D, P, P, P, P, F32, I32, P, SZ, P, P, P],
         "mla_decode_plan": [D, P, I32, P, SZ, P],
@@ -153,6 +155,30 @@ def mla_decode_num_splits(dims, max_seq_len: int, total_tokens: int) -> int:
     _check("mla_decode_num_splits", load().mla_decode_num_splits(ctypes.byref(dims), int(max_seq_len),
                                                                  int(total_tokens), ctypes.byref(out)))
     return out.value
+
+
+def _choose(fn: str, dims, seq_lens_host, max_seq_len: int) -> int:
+    import numpy as np
+
+    out = ctypes.c_int32(0)
+    arr = None
+    ptr = None
+    if seq_lens_host is not None:
+        arr = np.ascontiguousarray(seq_lens_host, dtype=np.int32)
+        if arr.shape != (dims.batch,):
+            raise ValueError(f"seq_lens_host must be a host array of {dims.batch} int32 lengths")
+        ptr = arr.ctypes.data_as(ctypes.c_void_p)
+    _check(fn, getattr(load(), fn)(ctypes.byref(dims), ptr, int(max_seq_len), ctypes.byref(out)))
+    return out.value
+
+
+def mla_choose_splits(dims, seq_lens_host=None, max_seq_len: int = 0) -> int:
+    """Split count from host lengths (a numpy array or list of B int32), or from max_seq_len alone."""
+    return _choose("mla_choose_splits", dims, seq_lens_host, max_seq_len)
+
+
+def mla_choose_splits_fp8(dims, seq_lens_host=None, max_seq_len: int = 0) -> int:
+    return _choose("mla_choose_splits_fp8", dims, seq_lens_host, max_seq_len)
 
 
 def mla_decode_workspace_bytes(dims, num_splits: int) -> int:

@@ -129,6 +129,7 @@ const char* mla_status_str(int s) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARG: return "invalid argument";
     case MLA_ERR_UNSUPPORTED: return "unsupported dimensions or dtype";
+    case MLA_ERR_WORKSPACE: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -184,7 +185,7 @@ int check_decode_common(const mla_dims* d, int32_t num_splits, const void* works
   if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
   size_t need = 0;
   mla_decode_workspace_bytes(d, num_splits, &need);
-  if (workspace_bytes < need) return MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
   return MLA_OK;
 }
 
@@ -269,6 +270,42 @@ int decode_impl(const mla_dims* d, const void* q_cat, const void* kv_cache, cons
 
 int mla_decode_num_splits(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits) {
   return num_splits_impl(d, max_seq_len, total_tokens, num_splits, false);
+}
+
+namespace {
+
+// Longest sequence and total tokens from host lengths (each clamped into
+// [0, MB * block_size]), or a batch of max_seq_len-long sequences.
+int choose_splits_impl(const mla_dims* d, const int32_t* lens, int32_t max_seq_len, int32_t* num_splits, bool fp8) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (num_splits == nullptr) return MLA_ERR_INVALID_ARG;
+  int64_t total = 0;
+  int32_t mx = 0;
+  if (lens != nullptr) {
+    const int64_t cap = (int64_t)d->max_blocks_per_seq * d->block_size;
+    for (int b = 0; b < d->batch; ++b) {
+      const int64_t L = lens[b] < 0 ? 0 : (lens[b] > cap ? cap : lens[b]);
+      total += L;
+      if (L > mx) mx = (int32_t)L;
+    }
+  } else {
+    mx = max_seq_len;
+    total = (int64_t)d->batch * max_seq_len;
+  }
+  if (mx < 1) return MLA_ERR_INVALID_ARG;
+  return num_splits_impl(d, mx, total, num_splits, fp8);
+}
+
+}  // namespace
+
+int mla_choose_splits(const mla_dims* d, const int32_t* seq_lens_host, int32_t max_seq_len, int32_t* num_splits) {
+  return choose_splits_impl(d, seq_lens_host, max_seq_len, num_splits, false);
+}
+
+int mla_choose_splits_fp8(const mla_dims* d, const int32_t* seq_lens_host, int32_t max_seq_len,
+                          int32_t* num_splits) {
+  return choose_splits_impl(d, seq_lens_host, max_seq_len, num_splits, true);
 }
 
 int mla_decode_plan(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,
@@ -378,7 +415,8 @@ int cache_append_impl(const mla_dims* d, int32_t d_model, const void* h, const v
   if (!(rope_base > 0.f) || rope_base == INFINITY) return MLA_ERR_INVALID_ARG;
   size_t need = 0;
   mla_cache_append_workspace_bytes(d, d_model, &need);
-  if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need)) return MLA_ERR_INVALID_ARG;
+  if (need > 0 && !ptr_ok(workspace)) return MLA_ERR_INVALID_ARG;
+  if (need > 0 && workspace_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (!force_generic() && mla::append_mfma_supported(*d, d_model)) {
     int cus = 0;
@@ -429,10 +467,12 @@ int mla_prefill(const mla_dims* d, int32_t total_tokens, int32_t max_seqlen, con
     return MLA_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || softmax_scale == INFINITY) return MLA_ERR_INVALID_ARG;
   const mla::PrefillLayout lay = mla::prefill_layout(*d, total_tokens);
-  if (workspace_bytes < (size_t)lay.total_bytes) return MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < (size_t)lay.total_bytes) return MLA_ERR_WORKSPACE;
   const bool mfma = !force_generic() && mla::prefill_mfma_supported(*d);
-  // the matrix-core kernels address the workspace with 32-bit byte offsets
+  // the matrix-core kernels address the workspace with 32-bit byte offsets,
+  // and the attention grid's thread count must fit 32 bits
   if (mfma && lay.total_bytes >= ((int64_t)1 << 32)) return MLA_ERR_UNSUPPORTED;
+  if (mfma && !mla::prefill_grid_fits(*d, max_seqlen)) return MLA_ERR_UNSUPPORTED;
   return to_status(mla::launch_prefill(*d, total_tokens, max_seqlen, cu_seqlens, q_nope, q_rope, c_kv, k_rope, w_uk,
                                        w_uv, softmax_scale, causal, out, lse, workspace, mfma, (hipStream_t)stream));
 }
@@ -493,7 +533,8 @@ int mla_fused_output(const mla_dims* d, int32_t d_out, const float* o_latent, co
   if ((int64_t)d->batch * d->q_len > kMaxFusedRows) return MLA_ERR_UNSUPPORTED;
   size_t need = 0;
   mla_fused_output_workspace_bytes(d, d_out, &need);
-  if (need > 0 && (!ptr_ok(workspace) || workspace_bytes < need)) return MLA_ERR_INVALID_ARG;
+  if (need > 0 && !ptr_ok(workspace)) return MLA_ERR_INVALID_ARG;
+  if (need > 0 && workspace_bytes < need) return MLA_ERR_WORKSPACE;
   const bool packed = mla::fused_output_mfma_supported(*d, d_out);
   const bool mfma = packed && !force_generic();
   int cus = 1;

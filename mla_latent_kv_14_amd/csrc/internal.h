@@ -64,6 +64,9 @@ struct PrefillLayout {
 };
 bool prefill_mfma_supported(const mla_dims& d);
 PrefillLayout prefill_layout(const mla_dims& d, int64_t tokens);
+// whether the matrix-core attention grid for this batch and longest sequence
+// stays within 2^32 - 1 threads
+bool prefill_grid_fits(const mla_dims& d, int max_seqlen);
 hipError_t launch_prefill(const mla_dims& d, int tokens, int max_seqlen, const int32_t* cu, const void* q_nope,
                           const void* q_rope, const void* c_kv, const void* k_rope, const void* w_uk,
                           const void* w_uv, float scale, int causal, void* out, float* lse, void* ws, bool mfma,

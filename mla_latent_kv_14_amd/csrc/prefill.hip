@@ -623,6 +623,11 @@ bool prefill_mfma_supported(const mla_dims& d) {
   return d.dtype == MLA_BF16 && d.d_c == kDcP && d.d_rope == kDrP && d.d_nope == kDnP && d.d_v == kDnP;
 }
 
+bool prefill_grid_fits(const mla_dims& d, int max_seqlen) {
+  const int64_t blocks = (int64_t)d.batch * d.num_heads * ((max_seqlen + kQB - 1) / kQB);
+  return blocks * kAThreads <= (int64_t)0xffffffffu;
+}
+
 // Workspace regions in elements of the storage type (each 256-B aligned).
 PrefillLayout prefill_layout(const mla_dims& d, int64_t tokens) {
   const int64_t esz = d.dtype == MLA_F32 ? 4 : 2;
