@@ -5,7 +5,7 @@ relative L2 1e-2, plus two checks derived from the arithmetic:
   * every element lies within half a bf16 step of the oracle plus the
     float32 summation bound K 2^-24 sum_k |h_k| |w_k| (any order of K
     additions; for RoPE columns the bounds of both pair members add);
-  * at least 95% of the elements equal the oracle rounded to bf16 (only
+  * at least 99.5% of the elements equal the oracle rounded to bf16 (only
     values within the summation error of a rounding midpoint may differ).
 Every other cache element must be bit-identical to what was there before.
 """
@@ -68,7 +68,7 @@ def _check_rows(name, gpu_rows: torch.Tensor, ref_rows: np.ndarray, dtype: str, 
     if dtype == "bf16":
         exact = float((gpu_rows.view(torch.int16) == _bf16_round(ref_rows).view(torch.int16)).float().mean())
         say(f"  {name}: {100 * exact:.2f}% equal to the rounded oracle")
-        assert exact >= 0.95, f"{name}: only {exact:.3f} of the elements round like the oracle"
+        assert exact >= 0.995, f"{name}: only {exact:.4f} of the elements round like the oracle"
         if bound is not None:
             lim = _bf16_half_step(ref_rows) + bound
             worst = float(np.max(np.abs(g - ref_rows) / lim))
@@ -181,7 +181,7 @@ def test_append_portable_and_mfma_agree(monkeypatch):
     m, _ = metrics(to64(a), to64(b))
     same = float((a.view(torch.int16) == b.view(torch.int16)).float().mean())
     say(f"  mfma vs portable: max_abs={m:.3e}, {100 * same:.2f}% identical")
-    assert same >= 0.95
+    assert same >= 0.99  # each route rounds like the oracle in at least 99.5% of the elements
 
 
 # ------------------------------------------------------------------ positions far out

@@ -4,9 +4,9 @@ The oracle decodes the codes (kv_scale times each code's value, its own E4M3
 decoder) and runs the unchanged decode reference.  E4M3 values are exact in
 bf16 and float32, so the tolerances are those of the queries' storage type:
 float32 max-abs 1e-5; bf16 max-abs 2e-2 and relative L2 1e-2.  Small cases
-compare every element; full-size workloads compare sampled (sequence, head)
-pairs.  With kv_scale = 1 and one schedule the FP8 path must equal, bit for
-bit, the bf16 path run on a bf16 cache holding the same values.
+and the full-size workloads compare every element.  With kv_scale = 1 and
+one schedule the FP8 path must equal, bit for bit, the bf16 path run on a
+bf16 cache holding the same values.
 """
 from __future__ import annotations
 
@@ -188,31 +188,28 @@ def test_fp8_equals_bf16_cache_of_the_same_values(name, lens):
         assert torch.equal(a, b), what
 
 
-# ------------------------------------------------------------------ full size, sampled
+# ------------------------------------------------------------------ full size, every element
 
-def _sampled_check(name, pairs, seed=None):
+def _full_size_check(name, seed=None):
     wl = workload(name)
     p = make_problem(wl, seed)
-    say(f"case {name} full size: B={wl.batch} tokens={p.total_tokens} pairs={pairs}")
+    say(f"case {name} full size: seed={p.seed} B={wl.batch} tokens={p.total_tokens}")
     r = _run(p, fused=True)
     u_gpu = to64(r.u)
-    assert np.isfinite(u_gpu).all()
-    u_ref, _, _ = _oracle(p, select=pairs)
-    got = np.stack([u_gpu[b, :, h] for b, h in pairs])
-    ref = np.stack([u_ref[b, :, h] for b, h in pairs])
-    assert_parity(got, ref, wl.dtype, f"u sampled {name}")
+    u_ref, _, _ = _oracle(p)
+    assert_parity(u_gpu, u_ref, wl.dtype, f"u {name} (every element)")
 
 
 def test_fp8_full_single_4k():
-    _sampled_check("single_4k_fp8", [(0, 0), (0, 77), (0, 127)])
+    _full_size_check("single_4k_fp8")
 
 
 def test_fp8_full_batch64_1k8k():
-    _sampled_check("batch64_1k8k_fp8", [(0, 0), (7, 5), (31, 100), (63, 127), (40, 64)])
+    _full_size_check("batch64_1k8k_fp8")
 
 
 def test_fp8_full_mtp2_lognormal():
-    _sampled_check("mtp2_lognormal_fp8", [(0, 0), (17, 15), (64, 7), (127, 3)])
+    _full_size_check("mtp2_lognormal_fp8")
 
 
 # ------------------------------------------------------------------ FP8 append
@@ -271,7 +268,7 @@ def _append_fp8_check(prob):
     lim = _e4m3_half_step(v64) + _sum_bound(app, h, wl.d_c) / prob.kv_scale
     worst = float(np.max(np.abs(orc.e4m3_decode(got) - v64) / lim))
     say(f"  codes equal to the oracle's float32 decision: {100 * exact:.3f}%; worst error / bound = {worst:.3f}")
-    assert exact >= 0.95
+    assert exact >= 0.995
     assert worst <= 1.0
     mask = torch.ones(before.shape[:2], dtype=torch.bool, device=before.device)
     mask[blk, slot] = False
