@@ -4,21 +4,36 @@
 A step is one pass of the whole hot path over one batch: plan, absorb_q,
 split-KV attention, then the log-sum-exp combine and absorb_out (one fused
 call), for every sequence of the workload.  Inputs are seeded synthetic
-tensors already resident in HBM.  The same line also reports, measured on
-their own: the cache append of the step's new tokens and the prefill of a
-4 x 4096-token batch (--no-prefill skips it), the step over the workload's
-FP8-cache twin (--no-fp8), and the offline weight folds with the fused
-products that replace absorb_q and absorb_out (--no-folds).
+tensors already resident in HBM.
+
+Timing is cold: before every timed step (or call) a flush kernel reads
+1 GiB of an unrelated buffer, outside the timed events, so that the 256 MB
+last-level cache and the L2s hold none of the step's data (and no dirty
+lines) and the cache rows come from HBM.  Per-step (per-call) times come
+from HIP events on the library's stream; the line reports their mean (which
+`value` uses), p10, p50 and p90.  The attention kernel's roofline uses its
+cold mean without the event pair's own cost (back-to-back flush + kernel
+pairs minus back-to-back flushes).  Warm back-to-back numbers are reported
+separately and labelled as such.
+
+The line also carries: the roofs this chip sustains, measured by the
+measurement kernels of libmla_roofs.so (a streaming HBM read over 4 GiB and a
+register-only bf16 matrix-core loop), next to the published peaks; the
+attention kernel's roofline against both; the other decode workloads (one
+sequence of 4096, four of 131,072, and the 2-token batch of 128 at 16 heads)
+timed the same way; and, measured on their own, the cache append, the
+prefill of 4 x 4096 tokens (--no-prefill), the step over the FP8-cache twin
+(--no-fp8) and the weight folds with their fused products (--no-folds).
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-prefill]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-configs]
+                    [--cold-only] [--no-prefill] [--no-fp8] [--no-folds]
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -29,8 +44,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "batch64_1k8k_bf16"
+OTHER_WORKLOADS = ["single_4k_bf16", "long128k_bf16", "mtp2_lognormal_bf16"]
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FLUSH_BYTES = 1 << 30  # read before every cold timing: four times the 256 MB last-level cache
+READ_PEAK_BYTES = 4 << 30  # streamed by the HBM read measurement
 KERNEL_SOURCES = ["mla_latent_kv_14_amd/csrc/decode_mfma.hip", "mla_latent_kv_14_amd/csrc/common.h",
                   "mla_latent_kv_14_amd/csrc/mfma_util.h"]
 PREFILL_WORKLOAD = "prefill_4x4k_bf16"
@@ -62,11 +80,6 @@ def algorithmic_work(prob):
     visible = sum(int((L - wl.q_len + j + 1).sum()) for j in range(wl.q_len))
     flops = 2 * wl.heads * visible * (D + wl.d_c)
     return rows_bytes + q_bytes + table_bytes + o_bytes, flops
-
-
-def tokens_of(prob):
-    """New tokens one decode step produces: B * q_len."""
-    return prob.wl.batch * prob.wl.q_len
 
 
 def append_work(prob, d_model):
@@ -113,6 +126,208 @@ def measured_traffic(workload_name):
     return rec.get("bytes_per_launch")
 
 
+def stats(times_us):
+    a = np.asarray(times_us, dtype=np.float64)
+    return {"mean": float(a.mean()), "p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+class Timer:
+    """Cold and warm timing on one stream with HIP events (torch.cuda.Event records on the given stream).
+
+    The flush READS 1 GiB (plain loads, which allocate in the L2s and the last-level cache), so that the
+    caches hold only clean lines of an unrelated buffer.  A flush that writes would leave up to 288 MB of
+    dirty lines whose write-back lands inside the next timed kernel; write_flush = True does that, for
+    the comparison the line reports."""
+
+    def __init__(self, stream, flush_buf):
+        import torch
+        from mla_latent_kv_14_amd import roofs
+
+        self.torch, self.roofs = torch, roofs
+        self.stream, self.flush_buf = stream, flush_buf
+        self.sink = torch.zeros(max(roofs.read_grid(), 1) + 64, dtype=torch.int32, device=flush_buf.device)
+        self.write_flush = False
+
+    def flush(self):
+        if self.write_flush:
+            self.roofs.flush(self.flush_buf, self.stream)
+        else:
+            self.roofs.hbm_read(self.flush_buf, self.sink, False, self.stream)
+
+    def cold_mean(self, fn, n):
+        """Mean cold duration of fn without the event pair's own cost: n (flush, fn) pairs back to back
+        minus n flushes back to back, each between two events (us)."""
+        torch = self.torch
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        e[0].record(self.stream)
+        for _ in range(n):
+            self.flush()
+            fn()
+        e[1].record(self.stream)
+        e[2].record(self.stream)
+        for _ in range(n):
+            self.flush()
+        e[3].record(self.stream)
+        torch.cuda.synchronize()
+        return 1e3 * (e[0].elapsed_time(e[1]) - e[2].elapsed_time(e[3])) / n
+
+    def cold(self, fn, n):
+        """n calls of fn, each after a flush that is outside its events; returns the per-call times (us)."""
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            self.flush()
+            e0.record(self.stream)
+            fn()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return [1e3 * a.elapsed_time(b) for a, b in ev]
+
+    def cold_split(self, fns, n):
+        """n cold steps of the calls fns (flush, then an event between consecutive calls): per-call times."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for row in ev:
+            self.flush()
+            row[0].record(self.stream)
+            for k, fn in enumerate(fns):
+                fn()
+                row[k + 1].record(self.stream)
+        torch.cuda.synchronize()
+        return [[1e3 * row[k].elapsed_time(row[k + 1]) for row in ev] for k in range(len(fns))]
+
+    def warm(self, fn, n):
+        """n calls back to back between two events; returns the mean time per call (us)."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(n):
+            fn()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+
+def measure_roofs(timer):
+    """What the chip sustains: a cold streaming read of 4 GiB (plain and non-temporal loads, the faster
+    kept), a register-only bf16 matrix-core loop, and the cost of an event pair around an empty kernel."""
+    import torch
+    from mla_latent_kv_14_amd import roofs
+
+    dev = "cuda:0"
+    out = {}
+    try:
+        buf = torch.empty(READ_PEAK_BYTES // 4, dtype=torch.int32, device=dev)
+    except RuntimeError:
+        buf = torch.empty((READ_PEAK_BYTES // 4) // 4, dtype=torch.int32, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(max(roofs.read_grid(), 1) + 64, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * 4
+    best = 0.0
+    for nt in (False, True):
+        roofs.hbm_read(buf, sink, nt, timer.stream)  # warm-up of the code path
+        t = stats(timer.cold(lambda: roofs.hbm_read(buf, sink, nt, timer.stream), 5))
+        gbs = nbytes / (t["p50"] * 1e-6) / 1e9
+        out["hbm_read_nt" if nt else "hbm_read"] = {"bytes": nbytes, "us_p50": t["p50"], "gbs": gbs}
+        best = max(best, gbs)
+    out["hbm_read_gbs"] = best
+    del buf
+    msink = torch.zeros(roofs.mfma_grid() * 4 + 64, dtype=torch.int32, device=dev)
+    iters = 20000
+    flops = roofs.mfma_bf16(iters, msink, timer.stream)
+    t = stats(timer.cold(lambda: roofs.mfma_bf16(iters, msink, timer.stream), 5))
+    out["mfma_bf16"] = {"flops": flops, "us_p50": t["p50"], "tflops": flops / (t["p50"] * 1e-6) / 1e12}
+    out["mfma_bf16_tflops"] = out["mfma_bf16"]["tflops"]
+    e = stats(timer.cold(lambda: roofs.empty(timer.stream), 20))
+    out["event_pair_empty_kernel_us"] = e["p50"]
+    log(f"bench: roofs: HBM read {best:.0f} GB/s (spec {HBM_PEAK_GBS:.0f}), bf16 MFMA "
+        f"{out['mfma_bf16_tflops']:.0f} TFLOP/s (spec {MFMA_BF16_PEAK_TFLOPS:.0f}), event pair + empty kernel "
+        f"{e['p50']:.1f} us")
+    return out
+
+
+def roofline(alg_bytes, flops, kernel_us, peaks, traffic=None, kernel="mla_decode attention"):
+    """Both roofs for one kernel.  The bound is the roof whose floor is the longer time at the published
+    peaks (arithmetic intensity against the published ridge point); frac is against that roof's published
+    peak, frac_measured against what libmla_roofs measured on this chip."""
+    s = kernel_us * 1e-6
+    gbs = alg_bytes / s / 1e9
+    tflops = flops / s / 1e12
+    ai = flops / alg_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if ai < ridge else "mfma"
+    hbm_m, mfma_m = peaks.get("hbm_read_gbs"), peaks.get("mfma_bf16_tflops")
+    rec = {"kernel": kernel, "kernel_us": kernel_us, "bound": bound,
+           "achieved": gbs if bound == "hbm" else tflops,
+           "peak": HBM_PEAK_GBS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
+           "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "traffic": traffic,
+           "alg_bytes_per_launch": alg_bytes, "flops_per_launch": flops, "arith_intensity": ai,
+           "ridge_spec": ridge,
+           "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+           "hbm_frac_measured": gbs / hbm_m if hbm_m else None,
+           "mfma_tflops": tflops, "mfma_frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+           "mfma_frac_measured": tflops / mfma_m if mfma_m else None}
+    rec["frac"] = rec["hbm_frac"] if bound == "hbm" else rec["mfma_frac"]
+    rec["frac_measured"] = rec["hbm_frac_measured"] if bound == "hbm" else rec["mfma_frac_measured"]
+    return rec
+
+
+def measure_decode(prob, timer, K, warmup, peaks, cold_only=False, traffic=None, label=None):
+    """Cold steps, cold per-call breakdown, cold attention-kernel launches (and warm figures unless
+    cold_only) for one decode workload."""
+    import torch
+    from mla_latent_kv_14_amd.runner import DecodeRunner
+
+    wl = prob.wl
+    r = DecodeRunner(prob, device="cuda:0")
+    calls = [("plan", r.plan), ("absorb_q", r.absorb_q), ("decode", r.decode_planned),
+             ("combine_absorb_out", r.combine_absorb_out)]
+
+    def step():
+        for _, fn in calls:
+            fn()
+
+    for _ in range(warmup):
+        if cold_only:
+            timer.flush()
+        step()
+    torch.cuda.synchronize()
+    step_t = stats(timer.cold(step, K))
+    per_call = timer.cold_split([fn for _, fn in calls], K)
+    per_call = {n: stats(t) for (n, _), t in zip(calls, per_call)}
+    kern = stats(timer.cold(r.decode_planned, K))
+    kern_mean = timer.cold_mean(r.decode_planned, K)
+    alg_bytes, flops = algorithmic_work(prob)
+    rec = {"workload": label or wl.name, "batch": wl.batch, "heads": wl.heads, "q_len": wl.q_len,
+           "context_tokens": prob.total_tokens, "num_splits": r.num_splits,
+           "step_us": step_t, "per_call_us": per_call,
+           "attention_kernel_us": dict(kern, mean_without_events=kern_mean,
+                                       note="p10/p50/p90 of per-launch event pairs (each holds the event pair's own "
+                                            "cost); mean_without_events from back-to-back (flush, kernel) pairs "
+                                            "minus back-to-back flushes, used for the roofline"),
+           "tokens_per_s": wl.batch * wl.q_len / (step_t["mean"] * 1e-6),
+           "roofline": roofline(alg_bytes, flops, kern_mean, peaks, traffic)}
+    if not cold_only:
+        timer.write_flush = True
+        rec["attention_after_write_flush_us"] = timer.cold_mean(r.decode_planned, K)
+        timer.write_flush = False
+    if not cold_only:
+        rec["warm"] = {"step_us": timer.warm(step, K), "attention_kernel_us": timer.warm(r.decode_planned, K),
+                       "note": "back-to-back launches with caches warm; not used for any roofline figure"}
+    rl = rec["roofline"]
+    log(f"bench: {rec['workload']}: step {step_t['mean']:.1f} us cold (p10 {step_t['p10']:.1f}, p90 "
+        f"{step_t['p90']:.1f}); attention {kern_mean:.1f} us cold (events {kern['mean']:.1f}, after a write flush "
+        f"{rec.get('attention_after_write_flush_us', 0):.1f}) = {rl['hbm_gbs']:.0f} GB/s "
+        f"({100 * rl['hbm_frac']:.1f}% HBM spec, {100 * (rl['hbm_frac_measured'] or 0):.1f}% measured), "
+        f"{rl['mfma_tflops']:.0f} TFLOP/s ({100 * rl['mfma_frac']:.1f}% MFMA spec)")
+    return rec, r
+
+
 def cpu_baseline(prob, budget_s=15.0, max_s=30.0):
     """Time the float64 oracle on the first sequences of the same workload."""
     from oracle import mla_oracle as orc
@@ -151,8 +366,8 @@ def cpu_baseline(prob, budget_s=15.0, max_s=30.0):
 FOLD_D_IN = 1536  # query latent width: the input of the fused query weight
 
 
-def measure_folds(prob, r, stream, K, warmup):
-    """The offline folds and the fused products, with the unfolded route beside them.
+def measure_folds(prob, r, timer, K, warmup):
+    """The offline folds and the fused products, with the unfolded route beside them (cold calls).
 
     Fused query: q_cat = [W~_Q x ; q^R] replaces (W_in x, then absorb_q).
     Fused output: y = W~^O o replaces (absorb_out, then W^O u).  The unfolded
@@ -176,21 +391,11 @@ def measure_folds(prob, r, stream, K, warmup):
     wq = torch.empty((H, wl.d_c, fi.d_in), dtype=dt, device=dev)
     wo = torch.empty((fi.d_out, H * wl.d_c), dtype=dt, device=dev)
 
-    def timed(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return 1e3 * e0.elapsed_time(e1) / n
-
     fold_q = lambda: libmla.mla_fold_query_weight(d, fi.d_in, w_in, w_uk, wq)
     fold_o = lambda: libmla.mla_fold_output_weight(d, fi.d_out, w_o, w_uv, wo)
     fold_q()
     fold_o()
-    fold_q_us, fold_o_us = timed(fold_q, 2), timed(fold_o, 2)
+    fold_q_us, fold_o_us = stats(timer.cold(fold_q, 2))["mean"], stats(timer.cold(fold_o, 2))["mean"]
 
     q_cat = torch.empty((wl.batch, wl.q_len, H, D), dtype=dt, device=dev)
     ws = torch.empty((max(libmla.mla_fused_output_workspace_bytes(d, fi.d_out), 4) // 4,), dtype=torch.float32,
@@ -214,13 +419,13 @@ def measure_folds(prob, r, stream, K, warmup):
     for fn in (fq, fo, unfolded_q, unfolded_o):
         for _ in range(warmup):
             fn()
-    fq_us, fo_us = timed(fq, K), timed(fo, K)
-    uq_us, uo_us = timed(unfolded_q, K), timed(unfolded_o, K)
+    fq_us, fo_us = stats(timer.cold(fq, K))["mean"], stats(timer.cold(fo, K))["mean"]
+    uq_us, uo_us = stats(timer.cold(unfolded_q, K))["mean"], stats(timer.cold(unfolded_o, K))["mean"]
     esz = 2 if dt == torch.bfloat16 else 4
     q_bytes = wq.numel() * esz + x.numel() * esz + q_rope.numel() * esz + q_cat.numel() * esz
     o_bytes = wo.numel() * esz + o.numel() * 4 + y.numel() * esz
     res = {
-        "d_in": fi.d_in, "d_out": fi.d_out,
+        "d_in": fi.d_in, "d_out": fi.d_out, "timing": "cold",
         "fold_query_ms": fold_q_us / 1e3, "fold_output_ms": fold_o_us / 1e3,
         "fused_query": {"us": fq_us, "alg_bytes": q_bytes, "gbs": q_bytes / (fq_us * 1e-6) / 1e9,
                         "hbm_frac": q_bytes / (fq_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -240,12 +445,14 @@ def measure_folds(prob, r, stream, K, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true", help="time HIP-graph replays instead of eager launches")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other decode workloads")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="main workload only, every launch cold (warm-up included): for kernel traces")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-cache twin of the workload")
     ap.add_argument("--no-folds", action="store_true", help="skip the weight folds and fused products")
@@ -258,209 +465,129 @@ def main():
 
     import torch
 
-    from mla_latent_kv_14_amd.inputs import (WORKLOADS, make_append_inputs, make_fold_inputs, make_prefill_problem,
-                                             make_problem, workload)
-    from mla_latent_kv_14_amd.runner import DecodeRunner, PrefillRunner
+    from mla_latent_kv_14_amd.inputs import WORKLOADS, make_append_inputs, make_prefill_problem, make_problem, workload
+    from mla_latent_kv_14_amd.runner import PrefillRunner
 
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    timer = Timer(stream, flush_buf)
+    K, W = args.steps, args.warmup
+    cold_only = args.cold_only
+
+    peaks = {} if cold_only else measure_roofs(timer)
+
     wl = workload(args.workload)
     log(f"bench: generating {wl.name} ...")
     prob = make_problem(wl, args.seed)
-    r = DecodeRunner(prob, device="cuda:0")
-    stream = torch.cuda.current_stream()
+    traffic = measured_traffic(wl.name)
+    main_rec, r = measure_decode(prob, timer, K, W, peaks, cold_only=cold_only, traffic=traffic)
     log(f"bench: B={wl.batch} H={wl.heads} Lq={wl.q_len} tokens={prob.total_tokens} splits={r.num_splits}")
 
-    calls = [("plan", r.plan), ("absorb_q", r.absorb_q), ("decode", r.decode_planned),
-             ("combine_absorb_out", r.combine_absorb_out)]
-    for _ in range(args.warmup):
-        for _, fn in calls:
-            fn()
-    torch.cuda.synchronize()
-    log("bench: warmup done")
-    K = args.steps
+    configs = []
+    if not args.no_configs and not cold_only:
+        for name in OTHER_WORKLOADS:
+            if name == wl.name:
+                continue
+            p2 = make_problem(workload(name))
+            rec2, r2 = measure_decode(p2, timer, min(K, 20), min(W, 3), peaks)
+            configs.append(rec2)
+            del r2, p2
+            torch.cuda.empty_cache()
 
-    # per-call breakdown: eager calls bracketed by events on the library's stream
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-          for n, _ in calls}
-    for i in range(K):
-        for n, fn in calls:
-            ev[n][i][0].record(stream)
-            fn()
-            ev[n][i][1].record(stream)
-    torch.cuda.synchronize()
-    per_call_us = {n: 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n, _ in calls}
+    append = None
+    if not cold_only:
+        # the cache append (the step just before attention in a decode loop),
+        # timed on its own, cold; it rewrites the same slots every call
+        app = make_append_inputs(prob)
+        r.setup_append(app)
+        for _ in range(W):
+            r.cache_append()
+        at = stats(timer.cold(r.cache_append, K))
+        ap_bytes, ap_flops = append_work(prob, app.d_model)
+        append = {"us": at, "d_model": app.d_model, "alg_bytes": ap_bytes,
+                  "gbs": ap_bytes / (at["mean"] * 1e-6) / 1e9,
+                  "hbm_frac": ap_bytes / (at["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                  "tflops": ap_flops / (at["mean"] * 1e-6) / 1e12}
+        log(f"bench: cache append {at['mean']:.1f} us/call cold (d_model={app.d_model})")
 
-    # the timed region: K steps back to back, four eager launches per step with
-    # nothing between them (--graph replays HIP graphs of the same steps
-    # instead; on this stack that measured slower)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if not args.graph:
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(K):
-            for _, fn in calls:
-                fn()
-        end.record(stream)
-    else:
-        # one graph holds G consecutive steps; K/G replays run exactly K steps
-        G = max(d for d in range(1, min(K, 10) + 1) if K % d == 0)
-        g = r.capture(G)
-        g.replay()
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(K // G):
-            g.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / K
-    log(f"bench: {ms_step * 1e3:.1f} us/step ({'graph' if args.graph else 'eager'}); per call, eager (us): " +
-        ", ".join(f"{n}={v:.1f}" for n, v in per_call_us.items()))
-
-    # the attention kernel's own duration: K launches back to back between two
-    # events on its stream, so that each launch's dispatch overlaps the previous
-    # kernel (the per-call events above also hold that latency); the roofline
-    # below divides by this
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d0.record(stream)
-    for i in range(K):
-        r.decode_planned()
-    d1.record(stream)
-    torch.cuda.synchronize()
-    decode_kernel_us = 1e3 * d0.elapsed_time(d1) / K
-    log(f"bench: attention kernel {decode_kernel_us:.1f} us per launch (back to back)")
-
-    # the cache append (the step just before attention in a decode loop),
-    # timed on its own: K back-to-back calls; it rewrites the same slots
-    app = make_append_inputs(prob)
-    r.setup_append(app)
-    for _ in range(args.warmup):
-        r.cache_append()
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a0.record(stream)
-    for i in range(K):
-        r.cache_append()
-    a1.record(stream)
-    torch.cuda.synchronize()
-    append_us = 1e3 * a0.elapsed_time(a1) / K
-    ap_bytes, ap_flops = append_work(prob, app.d_model)
-    log(f"bench: cache append {append_us:.1f} us/call (d_model={app.d_model})")
-
-    # prefill (the non-absorbed forward over whole sequences), its own workload
     prefill = None
-    if not args.no_prefill:
+    if not args.no_prefill and not cold_only:
         pprob = make_prefill_problem(workload(PREFILL_WORKLOAD))
         pr = PrefillRunner(pprob, device="cuda:0")
         for _ in range(2):
             pr.prefill()
-        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        KP = 5
-        torch.cuda.synchronize()
-        p0.record(stream)
-        for i in range(KP):
-            pr.prefill()
-        p1.record(stream)
-        torch.cuda.synchronize()
-        pms = p0.elapsed_time(p1) / KP
+        pt = stats(timer.cold(pr.prefill, 5))
+        pms = pt["mean"] / 1e3
         f_attn, f_up = prefill_work(pprob)
         prefill = {"workload": PREFILL_WORKLOAD, "tokens": pprob.total_tokens, "heads": pprob.wl.heads,
-                   "causal": True, "ms_per_call": pms, "tokens_per_s": pprob.total_tokens / (pms * 1e-3),
+                   "causal": True, "ms_per_call": pms, "us": pt, "tokens_per_s": pprob.total_tokens / (pms * 1e-3),
                    "attn_tflop": f_attn / 1e12, "upproject_tflop": f_up / 1e12,
                    "tflops": (f_attn + f_up) / (pms * 1e-3) / 1e12,
-                   "mfma_frac": (f_attn + f_up) / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-        log(f"bench: prefill {PREFILL_WORKLOAD}: {pms:.2f} ms, {prefill['tflops']:.0f} TFLOP/s")
-        del pr
+                   "mfma_frac": (f_attn + f_up) / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                   "mfma_frac_measured": ((f_attn + f_up) / (pms * 1e-3) / 1e12 / peaks["mfma_bf16_tflops"]
+                                          if peaks.get("mfma_bf16_tflops") else None)}
+        log(f"bench: prefill {PREFILL_WORKLOAD}: {pms:.2f} ms cold, {prefill['tflops']:.0f} TFLOP/s")
+        del pr, pprob
+        torch.cuda.empty_cache()
 
-    # the same step over an FP8 (E4M3) cache: the workload's FP8 twin (same
-    # draws, codes of value / kv_scale)
     fp8 = None
     twin = wl.name.replace("_bf16", "_fp8")
-    if not args.no_fp8 and not prob.fp8 and twin in WORKLOADS:
+    if not args.no_fp8 and not cold_only and not prob.fp8 and twin in WORKLOADS:
         fprob = make_problem(workload(twin), args.seed)
-        fr = DecodeRunner(fprob, device="cuda:0")
-        fcalls = [fr.plan, fr.absorb_q, fr.decode_planned, fr.combine_absorb_out]
-        for _ in range(args.warmup):
-            for fn in fcalls:
-                fn()
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for i in range(K):
-            for fn in fcalls:
-                fn()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        f_step = f0.elapsed_time(f1) / K
-        torch.cuda.synchronize()
-        f0.record(stream)
-        for i in range(K):
-            fr.decode_planned()
-        f1.record(stream)
-        torch.cuda.synchronize()
-        f_kernel_us = 1e3 * f0.elapsed_time(f1) / K
-        f_bytes, _ = algorithmic_work(fprob)
-        fp8 = {"workload": twin, "kv_scale": fprob.kv_scale, "ms_per_step": f_step,
-               "tokens_per_s": tokens_of(fprob) / (f_step * 1e-3), "attention_kernel_us": f_kernel_us,
-               "alg_bytes_per_launch": f_bytes, "gbs": f_bytes / (f_kernel_us * 1e-6) / 1e9,
-               "hbm_frac": f_bytes / (f_kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-               "cache_bytes": int(fprob.cache.numel()), "num_splits": fr.num_splits}
-        log(f"bench: FP8 cache ({twin}): {f_step * 1e3:.1f} us/step, attention {f_kernel_us:.1f} us")
-        del fr
+        fp8, fr = measure_decode(fprob, timer, K, W, peaks)
+        fp8["kv_scale"] = fprob.kv_scale
+        fp8["cache_bytes"] = int(fprob.cache.numel())
+        del fr, fprob
+        torch.cuda.empty_cache()
 
     folds = None
-    if not args.no_folds:
-        folds = measure_folds(prob, r, stream, K, args.warmup)
-
-    alg_bytes, flops = algorithmic_work(prob)
-    dec_s = decode_kernel_us * 1e-6
-    achieved_gbs = alg_bytes / dec_s / 1e9
-    achieved_tflops = flops / dec_s / 1e12
-    tokens = wl.batch * wl.q_len
-    traffic = measured_traffic(wl.name)
+    if not args.no_folds and not cold_only:
+        folds = measure_folds(prob, r, timer, min(K, 20), W)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not cold_only:
         log("bench: timing the CPU oracle on a sample ...")
         cpu = cpu_baseline(prob)
 
+    ms_step = main_rec["step_us"]["mean"] / 1e3
+    tokens = wl.batch * wl.q_len
+    alg_bytes, flops = algorithmic_work(prob)
     rec = {
         "metric": "MLA decode tokens/s + TFLOP/s & HBM GB/s vs roofline, B=64 H=128 ctx 1K-8K",
         "value": tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": W,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
+        "timing": ("cold: a 1 GiB read flush before every timed step, outside its events; mean of per-step HIP "
+                   "event times"),
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_len": wl.q_len, "d_c": wl.d_c,
                    "d_rope": wl.d_rope, "d_nope": wl.d_nope, "d_v": wl.d_v, "block_size": wl.block_size,
                    "context_tokens": prob.total_tokens, "lengths": " ".join(str(x) for x in wl.lengths),
                    "num_splits": r.num_splits},
-        "roofline": {"kernel": "mla_decode attention", "kernel_us": decode_kernel_us, "bound": "hbm",
-                     "achieved": achieved_gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic, "alg_bytes_per_launch": alg_bytes,
-                     "mfma_tflops": achieved_tflops, "mfma_frac": achieved_tflops / MFMA_BF16_PEAK_TFLOPS},
-        "per_call_us": per_call_us,
-        "launch": "hip_graph" if args.graph else "eager",
+        "roofline": main_rec["roofline"],
+        "step_us": main_rec["step_us"],
+        "attention_kernel_us": main_rec["attention_kernel_us"],
+        "per_call_us": main_rec["per_call_us"],
+        "warm": main_rec.get("warm"),
         "step_tflops": flops / (ms_step * 1e-3) / 1e12,
         "step_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
+        "measured_roofs": peaks,
+        "configs": configs,
         "cpu_baseline": cpu,
         "prefill": prefill,
         "fp8_cache": fp8,
         "weight_folds": folds,
-        "cache_append": {"us_per_call": append_us, "d_model": app.d_model, "alg_bytes": ap_bytes,
-                         "gbs": ap_bytes / (append_us * 1e-6) / 1e9,
-                         "hbm_frac": ap_bytes / (append_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                         "tflops": ap_flops / (append_us * 1e-6) / 1e12},
+        "cache_append": append,
     }
     print(json.dumps(rec), flush=True)
 

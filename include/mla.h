@@ -136,8 +136,11 @@ int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t*
  *               (MLA_ERR_WORKSPACE if workspace_bytes is smaller), 16-byte
  *               aligned; overwritten by every call, so calls sharing one
  *               workspace must be ordered on one stream
- *   o_partial   [B,Lq,H,S,d_c] float32: o_s = sum_{t in split} p_t c_t with p
- *               normalised within the split
+ *   o_partial   [B,Lq,H,S,d_c] in the storage type (float32 or bf16): o_s =
+ *               sum_{t in split} p_t c_t with p normalised within the split,
+ *               rounded once to the storage type (these partials are the
+ *               largest write of the step; bf16 halves it, at a relative
+ *               error of 2^-9 per element, well inside the bf16 tolerances)
  *   lse_partial [B,Lq,H,S] float32: natural-log log-sum-exp of the split's
  *               scaled scores; -inf marks an unused or empty split, whose
  *               o_partial entry is left unwritten.
@@ -150,7 +153,7 @@ int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t*
  * that sequence is then meaningless). */
 int mla_decode(const mla_dims* dims, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
-               size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream);
+               size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream);
 
 /* First half of mla_decode: enqueue only the planner, which writes the work
  * schedule for seq_lens [B] int32 (device) and num_splits into the workspace.
@@ -164,7 +167,7 @@ int mla_decode_plan(const mla_dims* dims, const int32_t* seq_lens, int32_t num_s
  * Arguments as for mla_decode; num_splits must equal the planned value. */
 int mla_decode_planned(const mla_dims* dims, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                        float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
-                       float* o_partial, float* lse_partial, void* stream);
+                       void* o_partial, float* lse_partial, void* stream);
 
 /* ---- FP8 latent cache ---------------------------------------------------
  * The latent cache in FP8 ("Deconstructing DeepSeek V4 Pro", Practical
@@ -192,18 +195,18 @@ int mla_decode_plan_fp8(const mla_dims* dims, const int32_t* seq_lens, int32_t n
                         size_t workspace_bytes, void* stream);
 int mla_decode_planned_fp8(const mla_dims* dims, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
                            const int32_t* block_table, float softmax_scale, int32_t num_splits,
-                           const void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial,
+                           const void* workspace, size_t workspace_bytes, void* o_partial, float* lse_partial,
                            void* stream);
 int mla_decode_fp8(const mla_dims* dims, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
                    const int32_t* block_table, const int32_t* seq_lens, float softmax_scale, int32_t num_splits,
-                   void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream);
+                   void* workspace, size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream);
 
 /* Log-sum-exp merge of the splits (exact rewrite of one softmax over the
  * union of the splits' keys):
  *   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s
  * skipping splits with lse_s = -inf.  o_partial/lse_partial as written by
  * mla_decode; o_latent [B,Lq,H,d_c] float32; lse [B,Lq,H] float32 or NULL. */
-int mla_combine(const mla_dims* dims, int32_t num_splits, const float* o_partial, const float* lse_partial,
+int mla_combine(const mla_dims* dims, int32_t num_splits, const void* o_partial, const float* lse_partial,
                 float* o_latent, float* lse, void* stream);
 
 /* Apply W^UV after the latent-weighted sum ("DeepSeek-V3 MLA: Multi-Head
@@ -225,7 +228,7 @@ int mla_absorb_out(const mla_dims* dims, const float* o_latent, const void* w_uv
  * the merged latent output is only written if o_latent is given; otherwise the
  * call runs the two kernels and needs o_latent as their intermediate
  * (MLA_ERR_UNSUPPORTED if it is NULL). */
-int mla_combine_absorb_out(const mla_dims* dims, int32_t num_splits, const float* o_partial, const float* lse_partial,
+int mla_combine_absorb_out(const mla_dims* dims, int32_t num_splits, const void* o_partial, const float* lse_partial,
                            const void* w_uv, void* out, float* o_latent, float* lse, void* stream);
 
 /* 1 if mla_combine_absorb_out runs as one fused kernel for these dims and

@@ -201,7 +201,7 @@ def mla_decode(dims, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch), float(softmax_scale), int(num_splits),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
 
 
@@ -226,7 +226,7 @@ def mla_decode_planned(dims, q_cat, kv_cache, block_table, softmax_scale, num_sp
         _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D),
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq), float(softmax_scale),
         int(num_splits), ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
 
 
@@ -260,7 +260,7 @@ def mla_decode_planned_fp8(dims, q_cat, kv_cache, kv_scale, block_table, softmax
         _ptr(kv_cache, "kv_cache", torch.uint8, d.num_blocks * d.block_size * D), float(kv_scale),
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq), float(softmax_scale),
         int(num_splits), ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
 
 
@@ -277,7 +277,7 @@ def mla_decode_fp8(dims, q_cat, kv_cache, kv_scale, block_table, seq_lens, softm
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch), float(softmax_scale), int(num_splits),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-        _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
 
 
@@ -285,7 +285,7 @@ def mla_combine(dims, num_splits, o_partial, lse_partial, o_latent, lse=None, st
     d = dims
     rows = d.batch * d.q_len * d.num_heads
     _check("mla_combine", load().mla_combine(
-        ctypes.byref(d), int(num_splits), _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        ctypes.byref(d), int(num_splits), _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits),
         _ptr(o_latent, "o_latent", torch.float32, rows * d.d_c),
         _ptr(lse, "lse", torch.float32, rows) if lse is not None else None, _stream(stream)))
@@ -304,7 +304,7 @@ def mla_combine_absorb_out(dims, num_splits, o_partial, lse_partial, w_uv, out, 
     d, st = dims, _storage_dtype(dims)
     rows = d.batch * d.q_len * d.num_heads
     _check("mla_combine_absorb_out", load().mla_combine_absorb_out(
-        ctypes.byref(d), int(num_splits), _ptr(o_partial, "o_partial", torch.float32, rows * num_splits * d.d_c),
+        ctypes.byref(d), int(num_splits), _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits),
         _ptr(w_uv, "w_uv", st, d.num_heads * d.d_v * d.d_c), _ptr(out, "out", st, rows * d.d_v),
         _ptr(o_latent, "o_latent", torch.float32, rows * d.d_c) if o_latent is not None else None,

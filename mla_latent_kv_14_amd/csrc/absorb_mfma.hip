@@ -241,13 +241,14 @@ __global__ __launch_bounds__(kThreadsC) void absorb_out_mfma(const float* __rest
 // that the merged latent output never leaves the chip:
 //   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s,  u = W_UV[h] o.
 // grid (H, ceil(M / 32)), 8 waves.  The 32 rows of a workgroup are merged
-// straight into the bf16 hi/lo LDS tile of absorb_out_mfma; each thread owns
+// straight into the bf16 hi/lo LDS tile of absorb_out_mfma (the partials are
+// bf16, the merge is float32); each thread owns
 // 32 columns of one row and keeps two splits' loads in flight.  Splits with
 // lse_s = -inf are skipped (their o_s is never read).  o_latent and lse are
 // written when given.
 constexpr int kMaxFusedSplits = 64;
 
-__global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const float* __restrict__ o_part,
+__global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __restrict__ o_part,
                                                               const float* __restrict__ lse_part,
                                                               const uint16_t* __restrict__ w_uv,
                                                               uint16_t* __restrict__ out, float* __restrict__ o_latent,
@@ -280,20 +281,21 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const float* __res
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (m < M) {
-      const float4* src = reinterpret_cast<const float4*>(o_part + ((size_t)m * H + h) * S * kDC) + j;
-      auto fma4 = [&](float wgt, const float4* x) {
+      // bf16 partials: four columns (8 bytes) per load
+      const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)m * H + h) * S * kDC) + j;
+      auto fma4 = [&](float wgt, const uint2* x) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          acc[k].x = fmaf(wgt, x[k].x, acc[k].x);
-          acc[k].y = fmaf(wgt, x[k].y, acc[k].y);
-          acc[k].z = fmaf(wgt, x[k].z, acc[k].z);
-          acc[k].w = fmaf(wgt, x[k].w, acc[k].w);
+          acc[k].x = fmaf(wgt, __uint_as_float(x[k].x << 16), acc[k].x);
+          acc[k].y = fmaf(wgt, __uint_as_float(x[k].x & 0xffff0000u), acc[k].y);
+          acc[k].z = fmaf(wgt, __uint_as_float(x[k].y << 16), acc[k].z);
+          acc[k].w = fmaf(wgt, __uint_as_float(x[k].y & 0xffff0000u), acc[k].w);
         }
       };
       for (int s2 = 0; s2 < S; s2 += 2) {
         const float w0 = wts[r][s2];
         const float w1 = (s2 + 1 < S) ? wts[r][s2 + 1] : 0.f;
-        float4 x0[8], x1[8];
+        uint2 x0[8], x1[8];
         if (w0 != 0.f) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) x0[k] = src[(size_t)s2 * (kDC / 4) + 16 * k];
@@ -335,10 +337,11 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const voi
 
 int combine_out_max_splits() { return kMaxFusedSplits; }
 
-hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o_part, const float* lse_part,
+hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const void* o_part, const float* lse_part,
                                    const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream) {
   const int M = d.batch * d.q_len;
-  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreadsC), 0, stream, o_part, lse_part,
+  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreadsC), 0, stream,
+                     static_cast<const uint16_t*>(o_part), lse_part,
                      (const uint16_t*)w_uv, (uint16_t*)out, o_latent, lse, M, d.num_heads, splits);
   return hipGetLastError();
 }

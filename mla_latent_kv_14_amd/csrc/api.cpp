@@ -192,7 +192,7 @@ int check_decode_common(const mla_dims* d, int32_t num_splits, const void* works
 bool positive_finite(float x) { return x > 0.f && x == x && x != INFINITY; }
 
 int check_attention_args(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
-                         float softmax_scale, float* o_partial, float* lse_partial, bool fp8, float kv_scale) {
+                         float softmax_scale, void* o_partial, float* lse_partial, bool fp8, float kv_scale) {
   if (!ptr_ok(q_cat) || !ptr_ok(kv_cache) || !ptr_ok(block_table) || !ptr_ok(o_partial) || !ptr_ok(lse_partial))
     return MLA_ERR_INVALID_ARG;
   if (!positive_finite(softmax_scale)) return MLA_ERR_INVALID_ARG;
@@ -208,7 +208,7 @@ hipError_t enqueue_plan(const mla_dims& d, const int32_t* seq_lens, int32_t num_
 
 hipError_t enqueue_attention(const mla_dims& d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                              float softmax_scale, int32_t num_splits, const void* workspace, const DecodeShape& sh,
-                             float* o_partial, float* lse_partial, hipStream_t s, bool fp8, float kv_scale) {
+                             void* o_partial, float* lse_partial, hipStream_t s, bool fp8, float kv_scale) {
   const int32_t* ws = static_cast<const int32_t*>(workspace);
   const float kv = fp8 ? kv_scale : 1.f;
   switch (pick_decode(d)) {
@@ -235,7 +235,7 @@ int plan_impl(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, vo
 
 int planned_impl(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                  float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
-                 float* o_partial, float* lse_partial, void* stream, bool fp8, float kv_scale) {
+                 void* o_partial, float* lse_partial, void* stream, bool fp8, float kv_scale) {
   int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
   st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial, fp8, kv_scale);
@@ -249,7 +249,7 @@ int planned_impl(const mla_dims* d, const void* q_cat, const void* kv_cache, con
 
 int decode_impl(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                 const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
-                size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream, bool fp8,
+                size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream, bool fp8,
                 float kv_scale) {
   int st = check_decode_common(d, num_splits, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
@@ -315,14 +315,14 @@ int mla_decode_plan(const mla_dims* d, const int32_t* seq_lens, int32_t num_spli
 
 int mla_decode_planned(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                        float softmax_scale, int32_t num_splits, const void* workspace, size_t workspace_bytes,
-                       float* o_partial, float* lse_partial, void* stream) {
+                       void* o_partial, float* lse_partial, void* stream) {
   return planned_impl(d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, workspace_bytes,
                       o_partial, lse_partial, stream, false, 1.f);
 }
 
 int mla_decode(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
                const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
-               size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+               size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream) {
   return decode_impl(d, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
                      workspace_bytes, o_partial, lse_partial, stream, false, 1.f);
 }
@@ -338,19 +338,19 @@ int mla_decode_plan_fp8(const mla_dims* d, const int32_t* seq_lens, int32_t num_
 
 int mla_decode_planned_fp8(const mla_dims* d, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
                            const int32_t* block_table, float softmax_scale, int32_t num_splits, const void* workspace,
-                           size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+                           size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream) {
   return planned_impl(d, q_cat, kv_cache, block_table, softmax_scale, num_splits, workspace, workspace_bytes,
                       o_partial, lse_partial, stream, true, kv_scale);
 }
 
 int mla_decode_fp8(const mla_dims* d, const void* q_cat, const uint8_t* kv_cache, float kv_scale,
                    const int32_t* block_table, const int32_t* seq_lens, float softmax_scale, int32_t num_splits,
-                   void* workspace, size_t workspace_bytes, float* o_partial, float* lse_partial, void* stream) {
+                   void* workspace, size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream) {
   return decode_impl(d, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
                      workspace_bytes, o_partial, lse_partial, stream, true, kv_scale);
 }
 
-int mla_combine(const mla_dims* d, int32_t num_splits, const float* o_partial, const float* lse_partial,
+int mla_combine(const mla_dims* d, int32_t num_splits, const void* o_partial, const float* lse_partial,
                 float* o_latent, float* lse, void* stream) {
   int st = check_dims(d);
   if (st != MLA_OK) return st;
@@ -369,7 +369,7 @@ int mla_absorb_out(const mla_dims* d, const float* o_latent, const void* w_uv, v
   return to_status(mla::launch_absorb_out_generic(*d, o_latent, w_uv, out, (hipStream_t)stream));
 }
 
-int mla_combine_absorb_out(const mla_dims* d, int32_t num_splits, const float* o_partial, const float* lse_partial,
+int mla_combine_absorb_out(const mla_dims* d, int32_t num_splits, const void* o_partial, const float* lse_partial,
                            const void* w_uv, void* out, float* o_latent, float* lse, void* stream) {
   int st = check_dims(d);
   if (st != MLA_OK) return st;

@@ -40,7 +40,7 @@ struct DecodeArgs {
   const void* cache;
   const int32_t* block_table;
   const int32_t* ws;  // planner output
-  float* o_part;
+  void* o_part;  // [B,Lq,H,S,d_c] in the storage type
   float* lse_part;
   float scale;
   int32_t B, Lq, H, d_c, d_rope, block_size, max_blocks, num_blocks, splits;

@@ -225,10 +225,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       blk = min(max(blk, 0), a.num_blocks - 1);
       return cache + ((size_t)blk * a.block_size + (t % a.block_size)) * (F8 ? kF8Row : kRowBytes);
     };
-    auto dma_to = [&](const uint8_t* base, uint32_t dst, uint32_t stride, int i) {
+    // The cache rows are read exactly once, so the copies are marked
+    // non-temporal (measured 1-5 % faster from a cold cache, more when the
+    // caches hold dirty lines).  src is the lane's source offset (dma_src).
+    auto dma_at = [&](const uint8_t* base, uint32_t dst, uint32_t stride, int i, int src) {
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(dst + stride * i);
-      __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(dma_src(i)), "s"(base), "{m0}"(m0)
+      __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(src), "s"(base), "{m0}"(m0)
                        : "memory");
+    };
+    auto dma_to = [&](const uint8_t* base, uint32_t dst, uint32_t stride, int i) {
+      dma_at(base, dst, stride, i, dma_src(i));
     };
     // LDS byte address of the copy destination of sub-tile sub: its ring stage
     auto stage_addr = [&](int sub) -> uint32_t {
@@ -435,6 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         const uint8_t* conv_src = smem + kBufs * kSubBytes + ((i + 2) & 1) * kF8Sub;
         uint8_t* conv_dst = smem + buf_of(i + 2) * kSubBytes;
         uint4 conv_x = make_uint4(0, 0, 0, 0);
+        int src_next = 0;
 
         // masking of sub-tile i (rare: only where some row's last visible token falls inside)
         if (t0 + kSub > lim_all) {
@@ -540,7 +547,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
                        to_sink ? 0u : copy_stride, pc);
               }
             } else {
-              if (ks % 4 == 2) dma_to(copy_src, copy_dst, copy_stride, ks / 4);
+              // the source offset of a copy is computed one MFMA earlier, so
+              // that the copy never waits on its own address arithmetic
+              if (ks % 4 == 1) {
+                src_next = dma_src(ks / 4);
+                pin(src_next);
+              }
+              if (ks % 4 == 2) dma_at(copy_src, copy_dst, copy_stride, ks / 4, src_next);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -606,16 +619,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     if (row_ok) {
       const size_t prow = ((size_t)b * R + n) * S;
       if (l > 0.f) {
+        // o_s rounded once to bf16 (the storage type of the partials)
         const float inv = (F8 ? a.kv_scale : 1.f) / l;
-        float* op = a.o_part + (prow + seg.split) * kDC;
+        uint16_t* op = static_cast<uint16_t*>(a.o_part) + (prow + seg.split) * kDC;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int c0 = (cg * MB + mb) * 32 + 4 * hi;
 #pragma unroll
           for (int gg = 0; gg < 4; ++gg) {
-            float4 v = make_float4(o[mb][4 * gg] * inv, o[mb][4 * gg + 1] * inv, o[mb][4 * gg + 2] * inv,
-                                   o[mb][4 * gg + 3] * inv);
-            *reinterpret_cast<float4*>(op + c0 + 8 * gg) = v;
+            const uint2 v = make_uint2(pack_bf16(o[mb][4 * gg] * inv, o[mb][4 * gg + 1] * inv),
+                                       pack_bf16(o[mb][4 * gg + 2] * inv, o[mb][4 * gg + 3] * inv));
+            *reinterpret_cast<uint2*>(op + c0 + 8 * gg) = v;
           }
         }
         if (cg == 0 && hi == 0) a.lse_part[prow + seg.split] = (m + log2f(l)) * kLn2;
@@ -640,7 +654,7 @@ bool decode_mfma_supported(const mla_dims& d) {
 }
 
 hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
-                              const int32_t* ws, float scale, int splits, int grid, float* o_part, float* lse_part,
+                              const int32_t* ws, float scale, int splits, int grid, void* o_part, float* lse_part,
                               hipStream_t stream, bool fp8, float kv_scale) {
   DecodeArgs a{q_cat, cache, table, ws, o_part, lse_part, scale, d.batch, d.q_len, d.num_heads, d.d_c, d.d_rope,
                d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale};

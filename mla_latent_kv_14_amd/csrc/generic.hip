@@ -171,11 +171,11 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
     const size_t prow = ((size_t)(b * a.Lq + j) * a.H + h) * S;
     if (t_end > seg.tok_begin) {
       const float inv = kF8 ? kv / l : 1.f / l;
-      float* op = a.o_part + (prow + seg.split) * a.d_c;
+      T* op = static_cast<T*>(a.o_part) + (prow + seg.split) * a.d_c;  // partials in the storage type
 #pragma unroll
       for (int i = 0; i < kMaxCols / 64; ++i) {
         const int c = lane + 64 * i;
-        if (c < a.d_c) op[c] = acc[i] * inv;
+        if (c < a.d_c) Storage<T>::store(op + c, acc[i] * inv);
       }
       if (lane == 0) a.lse_part[prow + seg.split] = m + logf(l);
     } else if (lane == 0) {
@@ -188,7 +188,22 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  One wave per row.
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ o_part,
+// The partials o_s are in the storage type T; four consecutive columns are
+// read at a time.
+template <typename T> struct Four;
+template <> struct Four<float> {
+  __device__ __forceinline__ static float4 load(const float* p) { return *reinterpret_cast<const float4*>(p); }
+};
+template <> struct Four<uint16_t> {
+  __device__ __forceinline__ static float4 load(const uint16_t* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                       __uint_as_float(v.y & 0xffff0000u));
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__ o_part,
                                                            const float* __restrict__ lse_part, float* __restrict__ o,
                                                            float* __restrict__ lse, int rows, int S, int d_c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -203,14 +218,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
     if (lse && lane == 0) lse[row] = -INFINITY;
     return;
   }
-  const float4* src = reinterpret_cast<const float4*>(o_part + (size_t)row * S * d_c);
+  const T* src = o_part + (size_t)row * S * d_c;
   for (int c = lane; c < n4; c += 64) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s = 0; s < S; ++s) {
       const float ls = lp[s];
       if (ls == -INFINITY) continue;
       const float w = expf(ls - total);
-      const float4 v = src[(size_t)s * n4 + c];
+      const float4 v = Four<T>::load(src + (size_t)s * d_c + 4 * c);
       acc.x = fmaf(w, v.x, acc.x);
       acc.y = fmaf(w, v.y, acc.y);
       acc.z = fmaf(w, v.z, acc.z);
@@ -254,7 +269,7 @@ hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const vo
 }
 
 hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
-                                 const int32_t* ws, float scale, int splits, int grid, float* o_part,
+                                 const int32_t* ws, float scale, int splits, int grid, void* o_part,
                                  float* lse_part, hipStream_t stream, bool fp8, float kv_scale) {
   DecodeArgs a{q_cat, cache, table, ws, o_part, lse_part, scale, d.batch, d.q_len, d.num_heads, d.d_c, d.d_rope,
                d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale};
@@ -270,11 +285,15 @@ hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const voi
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const mla_dims& d, int splits, const float* o_part, const float* lse_part, float* o,
+hipError_t launch_combine(const mla_dims& d, int splits, const void* o_part, const float* lse_part, float* o,
                           float* lse, hipStream_t stream) {
   const int rows = d.batch * d.q_len * d.num_heads;
-  hipLaunchKernelGGL(combine_kernel, dim3((rows + 3) / 4), dim3(kThreads), 0, stream, o_part, lse_part, o, lse,
-                     rows, splits, d.d_c);
+  if (d.dtype == MLA_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((rows + 3) / 4), dim3(kThreads), 0, stream,
+                       static_cast<const float*>(o_part), lse_part, o, lse, rows, splits, d.d_c);
+  else
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(o_part), lse_part, o, lse, rows, splits, d.d_c);
   return hipGetLastError();
 }
 

@@ -16,10 +16,10 @@ hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, i
 hipError_t launch_absorb_q_generic(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
                                    void* q_cat, hipStream_t stream);
 hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
-                                 const int32_t* ws, float scale, int splits, int grid, float* o_part,
+                                 const int32_t* ws, float scale, int splits, int grid, void* o_part,
                                  float* lse_part, hipStream_t stream, bool fp8, float kv_scale);
 int decode_generic_rows_per_group();
-hipError_t launch_combine(const mla_dims& d, int splits, const float* o_part, const float* lse_part, float* o,
+hipError_t launch_combine(const mla_dims& d, int splits, const void* o_part, const float* lse_part, float* o,
                           float* lse, hipStream_t stream);
 hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const void* w_uv, void* out,
                                      hipStream_t stream);
@@ -28,7 +28,7 @@ hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const vo
 bool decode_mfma_supported(const mla_dims& d);
 // fp8: the cache holds E4M3 codes standing for kv_scale times their value
 hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
-                              const int32_t* ws, float scale, int splits, int grid, float* o_part, float* lse_part,
+                              const int32_t* ws, float scale, int splits, int grid, void* o_part, float* lse_part,
                               hipStream_t stream, bool fp8, float kv_scale);
 
 // matrix-core absorption GEMMs for bf16, d_nope = d_v = 128, d_c = 512 (absorb_mfma.hip)
@@ -40,7 +40,7 @@ hipError_t launch_absorb_out_mfma(const mla_dims& d, const float* o, const void*
 // fused log-sum-exp merge + W_UV product (same support as the MFMA absorb
 // kernels, and at most combine_out_max_splits() splits)
 int combine_out_max_splits();
-hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const float* o_part, const float* lse_part,
+hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const void* o_part, const float* lse_part,
                                    const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream);
 
 // cache append (append.hip): matrix-core split-K path for bf16 storage with

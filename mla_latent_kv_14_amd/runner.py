@@ -42,7 +42,7 @@ class DecodeRunner:
         self.q_cat = torch.empty((B, Lq, H, wl.d_c + wl.d_rope), dtype=st, device=dev)
         ws_bytes = libmla.mla_decode_workspace_bytes(self.dims, self.num_splits)
         self.workspace = torch.empty(ws_bytes // 4, dtype=torch.int32, device=dev)
-        self.o_partial = torch.empty((B, Lq, H, self.num_splits, wl.d_c), dtype=torch.float32, device=dev)
+        self.o_partial = torch.empty((B, Lq, H, self.num_splits, wl.d_c), dtype=st, device=dev)  # storage type
         self.lse_partial = torch.empty((B, Lq, H, self.num_splits), dtype=torch.float32, device=dev)
         self.o = torch.empty((B, Lq, H, wl.d_c), dtype=torch.float32, device=dev)
         self.lse = torch.empty((B, Lq, H), dtype=torch.float32, device=dev)

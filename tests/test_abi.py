@@ -374,3 +374,4 @@ def test_roofs_invalid_args():
     flops = ctypes.c_double(0)
     assert lib.mla_roofs_mfma_bf16(0, P(FAKE), 1 << 20, ctypes.byref(flops), None) == -1
     assert lib.mla_roofs_mfma_bf16(10, P(FAKE), 1 << 20, None, None) == -1
+

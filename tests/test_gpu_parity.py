@@ -241,7 +241,7 @@ def test_combine_against_oracle():
     S = 5
     r = DecodeRunner(p, num_splits=S)
     g = torch.Generator().manual_seed(4)
-    o_part = torch.randn(r.o_partial.shape, generator=g)
+    o_part = torch.randn(r.o_partial.shape, generator=g).to(r.o_partial.dtype)  # partials are in the storage type
     lse_part = torch.randn(r.lse_partial.shape, generator=g) * 3
     lse_part[0, 0, 0, :] = -math.inf  # a row with no keys at all
     lse_part[0, 0, 1, 1:3] = -math.inf  # some empty splits
