@@ -9,12 +9,12 @@ tensors already resident in HBM.
 Timing is cold: before every timed step (or call) a flush kernel reads
 1 GiB of an unrelated buffer, outside the timed events, so that the 256 MB
 last-level cache and the L2s hold none of the step's data (and no dirty
-lines) and the cache rows come from HBM.  Per-step (per-call) times come
-from HIP events on the library's stream; the line reports their mean (which
-`value` uses), p10, p50 and p90.  The attention kernel's roofline uses its
-cold mean without the event pair's own cost (back-to-back flush + kernel
-pairs minus back-to-back flushes).  Warm back-to-back numbers are reported
-separately and labelled as such.
+lines) and the cache rows come from HBM.  Times come from HIP events on
+the library's stream: per sample, (flush, step) minus a flush alone, each
+between two events, so that the event pair's own cost cancels; the line
+reports their mean (which `value` uses), p10, p50 and p90, for the step and
+for the attention kernel alone (whose mean the roofline uses).  Warm
+back-to-back numbers are reported separately and labelled as such.
 
 The line also carries: the roofs this chip sustains, measured by the
 measurement kernels of libmla_roofs.so (a streaming HBM read over 4 GiB and a
@@ -155,23 +155,25 @@ class Timer:
         else:
             self.roofs.hbm_read(self.flush_buf, self.sink, False, self.stream)
 
-    def cold_mean(self, fn, n):
-        """Mean cold duration of fn without the event pair's own cost: n (flush, fn) pairs back to back
-        minus n flushes back to back, each between two events (us)."""
+    def cold_net(self, fn, n):
+        """n cold samples of fn without the event pair's own cost (us): each sample times (flush, fn) and then a
+        flush alone, each between two events and each after a flush that leaves the caches clean, and takes the
+        difference."""
         torch = self.torch
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
         torch.cuda.synchronize()
-        e[0].record(self.stream)
-        for _ in range(n):
+        for e in ev:
+            self.flush()
+            e[0].record(self.stream)
             self.flush()
             fn()
-        e[1].record(self.stream)
-        e[2].record(self.stream)
-        for _ in range(n):
+            e[1].record(self.stream)
             self.flush()
-        e[3].record(self.stream)
+            e[2].record(self.stream)
+            self.flush()
+            e[3].record(self.stream)
         torch.cuda.synchronize()
-        return 1e3 * (e[0].elapsed_time(e[1]) - e[2].elapsed_time(e[3])) / n
+        return [1e3 * (e[0].elapsed_time(e[1]) - e[2].elapsed_time(e[3])) for e in ev]
 
     def cold(self, fn, n):
         """n calls of fn, each after a flush that is outside its events; returns the per-call times (us)."""
@@ -297,24 +299,26 @@ def measure_decode(prob, timer, K, warmup, peaks, cold_only=False, traffic=None,
             timer.flush()
         step()
     torch.cuda.synchronize()
-    step_t = stats(timer.cold(step, K))
+    step_t = stats(timer.cold_net(step, K))
     per_call = timer.cold_split([fn for _, fn in calls], K)
     per_call = {n: stats(t) for (n, _), t in zip(calls, per_call)}
     kern = stats(timer.cold(r.decode_planned, K))
-    kern_mean = timer.cold_mean(r.decode_planned, K)
+    kern_net = stats(timer.cold_net(r.decode_planned, K))
+    kern_mean = kern_net["mean"]
     alg_bytes, flops = algorithmic_work(prob)
     rec = {"workload": label or wl.name, "batch": wl.batch, "heads": wl.heads, "q_len": wl.q_len,
            "context_tokens": prob.total_tokens, "num_splits": r.num_splits,
            "step_us": step_t, "per_call_us": per_call,
-           "attention_kernel_us": dict(kern, mean_without_events=kern_mean,
-                                       note="p10/p50/p90 of per-launch event pairs (each holds the event pair's own "
-                                            "cost); mean_without_events from back-to-back (flush, kernel) pairs "
-                                            "minus back-to-back flushes, used for the roofline"),
+           "attention_kernel_us": dict(kern_net, with_event_pair=kern,
+                                       note="each sample: (flush, kernel) minus a flush alone, each between two "
+                                            "events and after a clean flush, so the event pair's own cost cancels; "
+                                            "its mean is the roofline's kernel time; with_event_pair: the kernel "
+                                            "alone between two events"),
            "tokens_per_s": wl.batch * wl.q_len / (step_t["mean"] * 1e-6),
            "roofline": roofline(alg_bytes, flops, kern_mean, peaks, traffic)}
     if not cold_only:
         timer.write_flush = True
-        rec["attention_after_write_flush_us"] = timer.cold_mean(r.decode_planned, K)
+        rec["attention_after_write_flush_us"] = stats(timer.cold(r.decode_planned, K))["mean"]
         timer.write_flush = False
     if not cold_only:
         rec["warm"] = {"step_us": timer.warm(step, K), "attention_kernel_us": timer.warm(r.decode_planned, K),
@@ -568,8 +572,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "timing": ("cold: a 1 GiB read flush before every timed step, outside its events; mean of per-step HIP "
-                   "event times"),
+        "timing": ("cold: a 1 GiB read flush before every timed step; per step, (flush, step) minus a flush alone, "
+                   "each between two HIP events on the library's stream; value = tokens / mean"),
         "config": {"workload": wl.name, "batch": wl.batch, "heads": wl.heads, "q_len": wl.q_len, "d_c": wl.d_c,
                    "d_rope": wl.d_rope, "d_nope": wl.d_nope, "d_v": wl.d_v, "block_size": wl.block_size,
                    "context_tokens": prob.total_tokens, "lengths": " ".join(str(x) for x in wl.lengths),
