@@ -643,6 +643,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     tv = tv_next;
     have = have_next;
   }
+  // The last sub-tiles' copies into the sink may still be in flight: let them
+  // land before the workgroup's LDS is handed to another workgroup.
+  vm_wait<0>();
 }
 
 }  // namespace
