@@ -155,6 +155,21 @@ int mla_decode(const mla_dims* dims, const void* q_cat, const void* kv_cache, co
                const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* workspace,
                size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream);
 
+/* mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same planner and attention kernels, with the work schedule kept in a
+ * library-owned device array instead of a caller workspace.  The array holds
+ * the schedule of up to 65536 sequences (about 512 KiB); each GPU the library
+ * runs on keeps its own copy until the process ends.  Arguments and results
+ * are those of mla_decode without workspace/workspace_bytes.  The call
+ * allocates nothing.  MLA_ERR_WORKSPACE when dims->batch > 65536; the other
+ * statuses as for mla_decode.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (several streams, several threads) race
+ * and must be ordered by the caller, e.g. issued on one stream. */
+int mla_decode_noalloc(const mla_dims* dims, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* o_partial,
+                       float* lse_partial, void* stream);
+
 /* First half of mla_decode: enqueue only the planner, which writes the work
  * schedule for seq_lens [B] int32 (device) and num_splits into the workspace.
  * One plan serves every later mla_decode_planned call with the same dims,

@@ -58,6 +58,7 @@ def load() -> ctypes.CDLL:
         "mla_choose_splits_fp8": [D, P, I32, ctypes.POINTER(I32)],
         "mla_decode_workspace_bytes": [D, I32, ctypes.POINTER(SZ)],
         "mla_decode": [D, P, P, P, P, F32, I32, P, SZ, P, P, P],
+        "mla_decode_noalloc": [D, P, P, P, P, F32, I32, P, P, P],
         "mla_decode_plan": [D, P, I32, P, SZ, P],
         "mla_decode_planned": [D, P, P, P, F32, I32, P, SZ, P, P, P],
         "mla_decode_num_splits_fp8": [D, I32, I64, ctypes.POINTER(I32)],
@@ -201,6 +202,20 @@ def mla_decode(dims, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_
         _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
         _ptr(seq_lens, "seq_lens", torch.int32, d.batch), float(softmax_scale), int(num_splits),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+        _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
+        _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
+
+
+def mla_decode_noalloc(dims, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, o_partial,
+                       lse_partial, stream=None):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    D = d.d_c + d.d_rope
+    _check("mla_decode_noalloc", load().mla_decode_noalloc(
+        ctypes.byref(d), _ptr(q_cat, "q_cat", st, rows * D),
+        _ptr(kv_cache, "kv_cache", st, d.num_blocks * d.block_size * D),
+        _ptr(block_table, "block_table", torch.int32, d.batch * d.max_blocks_per_seq),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch), float(softmax_scale), int(num_splits),
         _ptr(o_partial, "o_partial", _storage_dtype(d), rows * num_splits * d.d_c),
         _ptr(lse_partial, "lse_partial", torch.float32, rows * num_splits), _stream(stream)))
 

@@ -120,6 +120,33 @@ int decode_shape(const mla_dims& d, bool fp8, DecodeShape* out) {
   return MLA_ERR_UNSUPPORTED;
 }
 
+// ---- allocation-free decode: the schedule lives in a file-scope device array
+//
+// Each GPU holds its own copy of `scratch` until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a stand-in
+// symbol): the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and only that address is
+// handed to the kernels.
+constexpr int kScratchMaxBatch = 65536;
+constexpr size_t kScratchWords = (size_t)mla::kWsHeader + 2 * (size_t)kScratchMaxBatch + 1;
+static __device__ __align__(256) int32_t scratch[kScratchWords];
+
+// Device address of this device's scratch (nullptr and MLA_ERR_HIP on failure).
+int scratch_address(int32_t** out) {
+  static std::mutex mu;
+  static int32_t* addr[kMaxDevices] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MLA_ERR_HIP;
+    addr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = addr[dev];
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -325,6 +352,31 @@ int mla_decode(const mla_dims* d, const void* q_cat, const void* kv_cache, const
                size_t workspace_bytes, void* o_partial, float* lse_partial, void* stream) {
   return decode_impl(d, q_cat, kv_cache, block_table, seq_lens, softmax_scale, num_splits, workspace,
                      workspace_bytes, o_partial, lse_partial, stream, false, 1.f);
+}
+
+int mla_decode_noalloc(const mla_dims* d, const void* q_cat, const void* kv_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, float softmax_scale, int32_t num_splits, void* o_partial,
+                       float* lse_partial, void* stream) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
+  if (!ptr_ok(seq_lens)) return MLA_ERR_INVALID_ARG;
+  st = check_attention_args(d, q_cat, kv_cache, block_table, softmax_scale, o_partial, lse_partial, false, 1.f);
+  if (st != MLA_OK) return st;
+  if (d->batch > kScratchMaxBatch) return MLA_ERR_WORKSPACE;
+  int32_t* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  DecodeShape sh;
+  st = decode_shape(*d, false, &sh);
+  if (st != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // the planner writes every schedule word the attention kernel reads, so
+  // nothing left from an earlier call needs clearing
+  hipError_t e = enqueue_plan(*d, seq_lens, num_splits, ws, sh, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return to_status(enqueue_attention(*d, q_cat, kv_cache, block_table, softmax_scale, num_splits, ws, sh, o_partial,
+                                     lse_partial, s, false, 1.f));
 }
 
 int mla_decode_num_splits_fp8(const mla_dims* d, int32_t max_seq_len, int64_t total_tokens, int32_t* num_splits) {

@@ -375,3 +375,17 @@ def test_roofs_invalid_args():
     assert lib.mla_roofs_mfma_bf16(0, P(FAKE), 1 << 20, ctypes.byref(flops), None) == -1
     assert lib.mla_roofs_mfma_bf16(10, P(FAKE), 1 << 20, None, None) == -1
 
+
+def test_decode_noalloc_host_checks():
+    """The allocation-free decode validates like mla_decode, and refuses batches past its array's capacity."""
+    def call(d, **over):
+        a = dict(q_cat=P(FAKE), cache=P(FAKE), table=P(FAKE), lens=P(FAKE), scale=0.1, splits=4, o=P(FAKE),
+                 lse=P(FAKE))
+        a.update(over)
+        return _call("mla_decode_noalloc", ctypes.byref(d), a["q_cat"], a["cache"], a["table"], a["lens"],
+                     ctypes.c_float(a["scale"]), a["splits"], a["o"], a["lse"], None)
+    d = _dims()
+    for over in ({"q_cat": None}, {"lens": None}, {"o": P(FAKE + 4)}, {"splits": 0}, {"scale": float("nan")}):
+        assert call(d, **over) == libmla.MLA_ERR_INVALID_ARG
+    assert call(_dims(batch=65537)) == libmla.MLA_ERR_WORKSPACE
+    assert call(_dims(dtype=9)) == libmla.MLA_ERR_UNSUPPORTED
