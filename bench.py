@@ -482,6 +482,12 @@ def main():
     cold_only = args.cold_only
 
     peaks = {} if cold_only else measure_roofs(timer)
+    if cold_only:
+        # two 1 GiB write flushes: a kernel of known write size beside the 1 GiB read flushes, so that
+        # HBM byte counters taken over this run can be calibrated
+        timer.roofs.flush(flush_buf, stream)
+        timer.roofs.flush(flush_buf, stream)
+        torch.cuda.synchronize()
 
     wl = workload(args.workload)
     log(f"bench: generating {wl.name} ...")
