@@ -220,7 +220,11 @@ int mla_decode_fp8(const mla_dims* dims, const void* q_cat, const uint8_t* kv_ca
  * union of the splits' keys):
  *   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s
  * skipping splits with lse_s = -inf.  o_partial/lse_partial as written by
- * mla_decode; o_latent [B,Lq,H,d_c] float32; lse [B,Lq,H] float32 or NULL. */
+ * mla_decode; o_latent [B,Lq,H,d_c] float32; lse [B,Lq,H] float32 or NULL.
+ * The float32 additions follow one fixed order (blocks of eight consecutive
+ * splits, and for batches under 32 token rows several block groups summed
+ * separately and then added in group order), which mla_combine_absorb_out
+ * follows too, so the two routes give identical bits. */
 int mla_combine(const mla_dims* dims, int32_t num_splits, const void* o_partial, const float* lse_partial,
                 float* o_latent, float* lse, void* stream);
 
@@ -247,8 +251,8 @@ int mla_combine_absorb_out(const mla_dims* dims, int32_t num_splits, const void*
                            const void* w_uv, void* out, float* o_latent, float* lse, void* stream);
 
 /* 1 if mla_combine_absorb_out runs as one fused kernel for these dims and
- * split count (bf16 storage, d_c = 512, d_nope = d_v = 128, at most 64
- * splits), else 0 (also for invalid arguments).  Host only. */
+ * split count (bf16 storage, d_c = 512, d_nope = d_v = 128, any split
+ * count), else 0 (also for invalid arguments).  Host only. */
 int mla_combine_absorb_out_fused(const mla_dims* dims, int32_t num_splits);
 
 /* ---- cache append: the step just before attention ---------------------- */

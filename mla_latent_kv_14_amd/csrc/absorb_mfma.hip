@@ -241,80 +241,105 @@ __global__ __launch_bounds__(kThreadsC) void absorb_out_mfma(const float* __rest
 // that the merged latent output never leaves the chip:
 //   lse = log sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) o_s,  u = W_UV[h] o.
 // grid (H, ceil(M / 32)), 8 waves.  The 32 rows of a workgroup are merged
-// straight into the bf16 hi/lo LDS tile of absorb_out_mfma (the partials are
-// bf16, the merge is float32); each thread owns
-// 32 columns of one row and keeps two splits' loads in flight.  Splits with
-// lse_s = -inf are skipped (their o_s is never read).  o_latent and lse are
-// written when given.
-constexpr int kMaxFusedSplits = 64;
-
+// into the bf16 hi/lo LDS tile of absorb_out_mfma (the partials are bf16, the
+// merge is float32).  Sixteen threads share a row, each owning 32 of its
+// columns.  A tile with fewer than 32 rows (small batches) gives each row P
+// = 2^merge_groups_log2(rows) groups of sixteen threads, which merge
+// interleaved blocks of eight splits side by side and add their sums through
+// LDS, in the merge order fixed beside merge_groups_log2 (common.h).  Each
+// thread keeps four splits' loads in flight; splits with lse_s = -inf are
+// skipped (their o_s is never read), and the weights are computed as the
+// splits are read, so any split count works.  o_latent and lse are written
+// when given.
 __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __restrict__ o_part,
                                                               const float* __restrict__ lse_part,
                                                               const uint16_t* __restrict__ w_uv,
                                                               uint16_t* __restrict__ out, float* __restrict__ o_latent,
                                                               float* __restrict__ lse_out, int M, int H, int S) {
   __shared__ __attribute__((aligned(16))) uint8_t ot[2][32 * kDC * 2];
-  __shared__ float wts[32][kMaxFusedSplits];
   __shared__ __attribute__((aligned(16))) float red[4][16][64];
+  __shared__ float4 gsum[32][8][16];  // [row group][column block][thread of the row], 64 KiB
   const int h = blockIdx.x, m0 = blockIdx.y * 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   WuvOperands op;
   wuv_request(w_uv, h, wave, lane, op);
 
-  // split weights: 16 lanes per row (two groups of 8 compute the same total)
-  {
-    const int r = tid >> 4, j = tid & 15, m = m0 + r;
-    const float* lp = lse_part + ((size_t)min(m, M - 1) * H + h) * S;
-    const float total = split_lse(lp, S, j & 7);
-    for (int s2 = j; s2 < S; s2 += 16) {
-      const float ls = lp[s2];
-      wts[r][s2] = (ls == -INFINITY || m >= M) ? 0.f : expf(ls - total);
-    }
-    if (lse_out != nullptr && j == 0 && m < M) lse_out[(size_t)m * H + h] = total;
-  }
-  __syncthreads();
+  const int rows = min(32, M - m0);
+  const int lgP = merge_groups_log2(rows), P = 1 << lgP;
+  const int g = tid >> 4, j = tid & 15;  // row group g = (row r, block lane p)
+  const int r = g >> lgP, p = g & (P - 1), m = m0 + r;
+  const bool valid = r < rows;
 
-  // merge: thread (row r, lane j of 16) owns float4 columns j + 16 k, k < 8
-  {
-    const int r = tid >> 4, j = tid & 15, m = m0 + r;
-    float4 acc[8];
+  float4 acc[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (m < M) {
-      // bf16 partials: four columns (8 bytes) per load
-      const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)m * H + h) * S * kDC) + j;
-      auto fma4 = [&](float wgt, const uint2* x) {
+  for (int k = 0; k < 8; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (valid) {
+    const float* lp = lse_part + ((size_t)m * H + h) * S;
+    const float total = split_lse(lp, S, j & 7);
+    if (lse_out != nullptr && p == 0 && j == 0) lse_out[(size_t)m * H + h] = total;
+    // bf16 partials: four columns (8 bytes) per load
+    const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)m * H + h) * S * kDC) + j;
+    auto fma4 = [&](float wgt, const uint2* x) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          acc[k].x = fmaf(wgt, __uint_as_float(x[k].x << 16), acc[k].x);
-          acc[k].y = fmaf(wgt, __uint_as_float(x[k].x & 0xffff0000u), acc[k].y);
-          acc[k].z = fmaf(wgt, __uint_as_float(x[k].y << 16), acc[k].z);
-          acc[k].w = fmaf(wgt, __uint_as_float(x[k].y & 0xffff0000u), acc[k].w);
-        }
-      };
-      for (int s2 = 0; s2 < S; s2 += 2) {
-        const float w0 = wts[r][s2];
-        const float w1 = (s2 + 1 < S) ? wts[r][s2 + 1] : 0.f;
-        uint2 x0[8], x1[8];
-        if (w0 != 0.f) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x0[k] = src[(size_t)s2 * (kDC / 4) + 16 * k];
-        }
-        if (w1 != 0.f) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) x1[k] = src[(size_t)(s2 + 1) * (kDC / 4) + 16 * k];
-        }
-        if (w0 != 0.f) fma4(w0, x0);
-        if (w1 != 0.f) fma4(w1, x1);
+      for (int k = 0; k < 8; ++k) {
+        acc[k].x = fmaf(wgt, __uint_as_float(x[k].x << 16), acc[k].x);
+        acc[k].y = fmaf(wgt, __uint_as_float(x[k].x & 0xffff0000u), acc[k].y);
+        acc[k].z = fmaf(wgt, __uint_as_float(x[k].y << 16), acc[k].z);
+        acc[k].w = fmaf(wgt, __uint_as_float(x[k].y & 0xffff0000u), acc[k].w);
       }
-      if (o_latent != nullptr) {
-        float4* dst = reinterpret_cast<float4*>(o_latent + ((size_t)m * H + h) * kDC) + j;
+    };
+    for (int blk = p; blk * kMergeBlock < S; blk += P) {
+      const int s_end = min(S, (blk + 1) * kMergeBlock);
+      for (int s0 = blk * kMergeBlock; s0 < s_end; s0 += 4) {
+        float wv[4];
+        uint2 x[4][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dst[16 * k] = acc[k];
+        for (int u = 0; u < 4; ++u) {
+          const float ls = (s0 + u < s_end) ? lp[s0 + u] : -INFINITY;
+          wv[u] = (ls == -INFINITY) ? 0.f : expf(ls - total);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (wv[u] != 0.f) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[u][k] = src[(size_t)(s0 + u) * (kDC / 4) + 16 * k];
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (wv[u] != 0.f) fma4(wv[u], x[u]);
       }
     }
+  }
+  // float4 column block k of thread j is columns 4 (j + 16 k) .. + 3
+  auto finish = [&](int k, const float4& v) {
+    if (valid && o_latent != nullptr)
+      reinterpret_cast<float4*>(o_latent + ((size_t)m * H + h) * kDC)[j + 16 * k] = v;
+    stage_hilo(ot, r, (j + 16 * k) >> 1, (j + 16 * k) & 1, v);
+  };
+  if (P == 1) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) stage_hilo(ot, r, (j + 16 * k) >> 1, (j + 16 * k) & 1, acc[k]);
+    for (int k = 0; k < 8; ++k) finish(k, acc[k]);
+  } else {
+    // the row's group sums, added left to right; group p finishes blocks k = p, p + P, ...
+#pragma unroll
+    for (int k = 0; k < 8; ++k) gsum[g][k][j] = acc[k];
+    __syncthreads();
+    for (int k = p; k < 8; k += P) {
+      float4 t = gsum[r << lgP][k][j];
+      for (int q = 1; q < P; ++q) {
+        const float4 y = gsum[(r << lgP) + q][k][j];
+        t.x += y.x;
+        t.y += y.y;
+        t.z += y.z;
+        t.w += y.w;
+      }
+      finish(k, valid ? t : make_float4(0.f, 0.f, 0.f, 0.f));
+    }
+    // rows past 32 / P have no threads: zero them (their products are never stored)
+    for (int rz = (32 >> lgP) + g; rz < 32; rz += 32)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        stage_hilo(ot, rz, (j + 16 * k) >> 1, (j + 16 * k) & 1, make_float4(0.f, 0.f, 0.f, 0.f));
   }
   __syncthreads();
   wuv_product(ot, red, op, wave, lane, m0, M, H, h, out);
@@ -334,8 +359,6 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const voi
                      d.num_heads, d.d_rope);
   return hipGetLastError();
 }
-
-int combine_out_max_splits() { return kMaxFusedSplits; }
 
 hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const void* o_part, const float* lse_part,
                                    const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream) {

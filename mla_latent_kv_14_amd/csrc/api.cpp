@@ -430,7 +430,7 @@ int mla_combine_absorb_out(const mla_dims* d, int32_t num_splits, const void* o_
     return MLA_ERR_INVALID_ARG;
   if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (!force_generic() && mla::absorb_mfma_supported(*d) && num_splits <= mla::combine_out_max_splits())
+  if (!force_generic() && mla::absorb_mfma_supported(*d))
     return to_status(mla::launch_combine_out_mfma(*d, num_splits, o_partial, lse_partial, w_uv, out, o_latent, lse, s));
   // two-kernel route: the merged latent output goes through o_latent
   if (o_latent == nullptr) return MLA_ERR_UNSUPPORTED;
@@ -607,7 +607,7 @@ int mla_fused_output_weight_packed(const mla_dims* d, int32_t d_out) {
 
 int mla_combine_absorb_out_fused(const mla_dims* d, int32_t num_splits) {
   if (check_dims(d) != MLA_OK || num_splits < 1 || num_splits > kMaxSplits) return 0;
-  return (!force_generic() && mla::absorb_mfma_supported(*d) && num_splits <= mla::combine_out_max_splits()) ? 1 : 0;
+  return (!force_generic() && mla::absorb_mfma_supported(*d)) ? 1 : 0;
 }
 
 }  // extern "C"

@@ -88,6 +88,21 @@ __device__ __forceinline__ float wave_sum(float v) {
 // fixed (eight strided partial sums combined by a butterfly; float addition
 // is commutative, so all eight lanes agree), which makes every kernel that
 // merges splits produce bit-identical weights exp(lse_s - lse).
+// Order of the merge o = sum_s w_s o_s, fixed so that every merge kernel
+// rounds alike.  Token rows are taken in tiles of 32 (m0 = m - m % 32, rows =
+// min(32, M - m0) of them); a tile of `rows` rows has P = 2^merge_groups_log2
+// groups per row (32 / P >= rows).  Split s lies in block s / kMergeBlock, and
+// block b in group b mod P.  Group p's sum C_p takes its splits in increasing
+// s, each by one fma (w_s o_s + C_p) starting from +0; then o = C_0 + C_1 +
+// ... + C_{P-1}, added left to right.  With P = 1 it is one sequential fma
+// chain over all splits.
+constexpr int kMergeBlock = 8;
+__host__ __device__ __forceinline__ int merge_groups_log2(int rows) {
+  int lg = 0;
+  while (lg < 5 && (32 >> (lg + 1)) >= rows) ++lg;
+  return lg;
+}
+
 __device__ __forceinline__ float split_lse(const float* lp, int S, int j) {
   float mx = -INFINITY;
   for (int s = j; s < S; s += 8) mx = fmaxf(mx, lp[s]);

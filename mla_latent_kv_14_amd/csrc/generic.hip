@@ -202,36 +202,50 @@ template <> struct Four<uint16_t> {
   }
 };
 
+// One wave per (token row m, head h) row: lane c owns float4 columns c, c +
+// 64, ...; the splits are added in the order merge_order fixes (common.h).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const T* __restrict__ o_part,
                                                            const float* __restrict__ lse_part, float* __restrict__ o,
-                                                           float* __restrict__ lse, int rows, int S, int d_c) {
+                                                           float* __restrict__ lse, int M, int H, int S, int d_c) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * (kThreads / 64) + wave;
-  if (row >= rows) return;
+  if (row >= M * H) return;
+  const int m = row / H;
+  const int lgP = merge_groups_log2(min(32, M - (m - m % 32))), P = 1 << lgP;
   const float* lp = lse_part + (size_t)row * S;
   const float total = split_lse(lp, S, lane & 7);
   float4* o4 = reinterpret_cast<float4*>(o + (size_t)row * d_c);
   const int n4 = d_c / 4;
-  if (total == -INFINITY) {
-    for (int c = lane; c < n4; c += 64) o4[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lse && lane == 0) lse[row] = -INFINITY;
-    return;
-  }
   const T* src = o_part + (size_t)row * S * d_c;
   for (int c = lane; c < n4; c += 64) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < S; ++s) {
-      const float ls = lp[s];
-      if (ls == -INFINITY) continue;
-      const float w = expf(ls - total);
-      const float4 v = Four<T>::load(src + (size_t)s * d_c + 4 * c);
-      acc.x = fmaf(w, v.x, acc.x);
-      acc.y = fmaf(w, v.y, acc.y);
-      acc.z = fmaf(w, v.z, acc.z);
-      acc.w = fmaf(w, v.w, acc.w);
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < P; ++p) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int blk = p; blk * kMergeBlock < S; blk += P) {
+        const int s_end = min(S, (blk + 1) * kMergeBlock);
+        for (int s = blk * kMergeBlock; s < s_end; ++s) {
+          const float ls = lp[s];
+          if (ls == -INFINITY) continue;
+          const float w = expf(ls - total);
+          if (w == 0.f) continue;
+          const float4 v = Four<T>::load(src + (size_t)s * d_c + 4 * c);
+          acc.x = fmaf(w, v.x, acc.x);
+          acc.y = fmaf(w, v.y, acc.y);
+          acc.z = fmaf(w, v.z, acc.z);
+          acc.w = fmaf(w, v.w, acc.w);
+        }
+      }
+      if (p == 0) {
+        sum = acc;
+      } else {
+        sum.x += acc.x;
+        sum.y += acc.y;
+        sum.z += acc.z;
+        sum.w += acc.w;
+      }
     }
-    o4[c] = acc;
+    o4[c] = sum;
   }
   if (lse && lane == 0) lse[row] = total;
 }
@@ -290,10 +304,12 @@ hipError_t launch_combine(const mla_dims& d, int splits, const void* o_part, con
   const int rows = d.batch * d.q_len * d.num_heads;
   if (d.dtype == MLA_F32)
     hipLaunchKernelGGL(combine_kernel<float>, dim3((rows + 3) / 4), dim3(kThreads), 0, stream,
-                       static_cast<const float*>(o_part), lse_part, o, lse, rows, splits, d.d_c);
+                       static_cast<const float*>(o_part), lse_part, o, lse, d.batch * d.q_len, d.num_heads, splits,
+                       d.d_c);
   else
     hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((rows + 3) / 4), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(o_part), lse_part, o, lse, rows, splits, d.d_c);
+                       static_cast<const uint16_t*>(o_part), lse_part, o, lse, d.batch * d.q_len, d.num_heads,
+                       splits, d.d_c);
   return hipGetLastError();
 }
 

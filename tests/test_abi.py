@@ -137,7 +137,9 @@ def test_combine_absorb_out_fused_predicate():
     d = _dims(dtype=libmla.MLA_BF16, num_heads=128, d_c=512, d_rope=64, d_nope=128, d_v=128, block_size=64)
     assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 8) == 1
     assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 64) == 1
-    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 65) == 0
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 65) == 1  # any split count
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 4096) == 1
+    assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 4097) == 0  # past the split limit: invalid
     assert lib.mla_combine_absorb_out_fused(ctypes.byref(d), 0) == 0
     d32 = _dims(dtype=0, d_c=64, d_rope=16, d_nope=32, d_v=32)
     assert lib.mla_combine_absorb_out_fused(ctypes.byref(d32), 8) == 0

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from mla_latent_kv_14_amd import binding as libmla
 from mla_latent_kv_14_amd.inputs import make_problem, workload
 from mla_latent_kv_14_amd.runner import DecodeRunner
 from oracle import mla_oracle as orc
@@ -233,6 +234,49 @@ def test_graph_replay_matches_eager():
     g.replay()
     torch.cuda.synchronize()
     assert torch.equal(r.u, u2)
+
+
+@pytest.mark.parametrize("batch,q_len,S", [(1, 1, 65), (1, 1, 9), (4, 1, 200), (5, 1, 17), (17, 1, 8), (8, 2, 33),
+                                          (64, 1, 8), (70, 1, 3)])
+def test_merge_row_groups_and_many_splits(batch, q_len, S):
+    """Merge of random partials for every tile shape of the merge kernels (1 to 32 rows per tile, so 32 to 1
+    block groups per row) and split counts past one block of eight: o and lse against the oracle's
+    log-sum-exp merge, and the fused merge + W_UV bit-identical to the two-kernel route."""
+    wl = workload("single_4k_bf16", batch=batch, q_len=q_len, heads=8, lengths=("fixed", (64,) * batch))
+    p = make_problem(wl, 44)
+    r = DecodeRunner(p, num_splits=S)
+    assert libmla.mla_combine_absorb_out_fused(r.dims, S) == 1
+    g = torch.Generator().manual_seed(S * 1000 + batch)
+    o_part = torch.randn(r.o_partial.shape, generator=g).to(r.o_partial.dtype)
+    lse_part = torch.randn(r.lse_partial.shape, generator=g) * 4
+    drop = torch.rand(r.lse_partial.shape, generator=g) < 0.2  # empty splits anywhere
+    lse_part[drop] = -math.inf
+    lse_part[0, 0, 0, :] = -math.inf  # a row with no keys
+    o_part[drop] = float("nan")  # never read
+    r.o_partial.copy_(o_part)
+    r.lse_partial.copy_(lse_part)
+    r.combine()
+    r.absorb_out()
+    torch.cuda.synchronize()
+    o1, l1, u1 = r.o.clone(), r.lse.clone(), r.u.clone()
+    o_ref, lse_ref = orc.lse_merge_reference(o_part.double().numpy(), lse_part.double().numpy())
+    got_o, got_l = to64(o1), to64(l1)
+    fin = np.isfinite(lse_ref)
+    assert np.all(np.isneginf(got_l[~fin])) and np.all(got_o[~fin] == 0)
+    err_l = np.abs(got_l[fin] - lse_ref[fin]).max()
+    err_o = np.abs(got_o - o_ref).max()
+    say(f"  merge B={batch} Lq={q_len} S={S}: lse max_abs {err_l:.2e}, o max_abs {err_o:.2e}")
+    assert err_l <= 1e-5 and err_o <= 1e-5
+    r.o.fill_(7.0)
+    r.lse.fill_(7.0)
+    r.u.fill_(0)
+    r.combine_absorb_out(keep_latent=True)
+    torch.cuda.synchronize()
+    assert torch.equal(r.o, o1) and torch.equal(r.lse, l1) and torch.equal(r.u, u1)
+    r.u.fill_(0)
+    r.combine_absorb_out()  # without the latent outputs
+    torch.cuda.synchronize()
+    assert torch.equal(r.u, u1)
 
 
 def test_combine_against_oracle():
