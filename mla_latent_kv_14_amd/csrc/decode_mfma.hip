@@ -40,15 +40,19 @@
 // FP8 cache (E4M3 codes, one scale per cache; "Deconstructing DeepSeek V4
 // Pro", Practical Deployment: the latent tolerates FP8): a 32-token sub-tile
 // is 18 KiB of contiguous codes, copied HBM -> LDS by the same copy engine
-// into one of two FP8 stages, and converted by the four waves into one of
-// three bf16 sub-tile buffers of the layout above (E4M3 values are exact in
-// bf16, so the matrix products see exactly the cached values), with rows past
-// the range zeroed; the score, softmax and latent-sum code is that of the
-// bf16 path.  The conversion of sub-tile i+2 runs inside the score loop of
-// sub-tile i+1, one 16-byte chunk of codes at a time, and each wave converts
-// exactly the chunks it copied itself, so once its reads have returned it
-// copies sub-tile i+4 into the same stage without waiting for the others.
-// The scale multiplies the softmax scale and the partial result.
+// into a ring of eight FP8 stages (seven sub-tiles ahead, as many bytes in
+// flight as the bf16 path).  A stage holds 16-code chunk c of token row r at
+// byte 512 c + 16 r, so both operand reads are contiguous over a wave: the
+// score operand (8 codes of one row) is a ds_read_b64, and the latent-sum
+// operand (8 tokens of one column) a ds_read_b64_tr_b8, the 8-bit transpose
+// read.  Each operand is converted to bf16 in registers right before its
+// MFMA (E4M3 values are exact in bf16, so the matrix products see exactly
+// the cached values and run in the same order as on a bf16 cache), and
+// nothing but the codes ever goes through LDS.  Rows past the range are
+// zeroed in the stage.  The scale multiplies the softmax scale and the
+// partial result.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -81,6 +85,8 @@ constexpr int kF8Sub = kSub * kF8Row;            // 18432
 constexpr int kF8Pieces = kF8Sub / 1024;         // 18
 constexpr int kF8DmaPerWave = 5;
 constexpr int kF8Chunks = kF8Sub / 16;           // 1152 16-byte chunks per sub-tile
+constexpr int kF8Stages = 8;                     // FP8 ring (144 KiB)
+constexpr int kF8Ahead = 7;                      // sub-tile i + 7 is copied while sub-tile i + 1 is scored
 
 // byte offset of (row, logical 16-B chunk) inside a sub-tile buffer
 __device__ __forceinline__ int tile_off(int r, int c) { return (r * kChunks + (c ^ swz(r))) * 16; }
@@ -115,12 +121,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
                                                                    const uint8_t* __restrict__ cache) {
   constexpr int CG = 4 / RG;   // waves sharing one group of 32 rows (split over O columns)
   constexpr int MB = 16 / CG;  // 32-column blocks of O per wave
-  // bf16 sub-tile buffers: the copy ring itself, or (FP8) two conversion
-  // targets followed by the ring of FP8 sub-tiles
-  constexpr int kBufs = F8 ? 3 : kStages;
-  constexpr int kF8Stages = 2;
+  // the copy ring: four bf16 sub-tiles, or eight FP8 ones
   constexpr int kDmaN = F8 ? kF8DmaPerWave : kDmaPerWave;  // copies per wave per sub-tile
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBufs * kSubBytes + (F8 ? kF8Stages * kF8Sub : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[F8 ? kF8Stages * kF8Sub : kStages * kSubBytes];
   // sink for the copies issued when there is no sub-tile left to fetch (so
   // that the score loop carries no per-step condition); never read
   __shared__ __attribute__((aligned(1024))) uint8_t sink[kThreads / 64 * 1024];
@@ -174,6 +177,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   }
   auto kbase = [&](int v) { return kbase_r[v]; };
   auto vbase = [&](int h, int par) { return vbase_r[h][par]; };
+  // FP8 stage offsets (16-code chunk c of row r at 512 c + 16 r):
+  //   score operand: codes 16 ks + 8 hi .. + 7 of row lane & 31 at
+  //     f8_kbase + 512 ks;
+  //   latent-sum operand (8-bit transpose read): in each group of 16 lanes,
+  //     lane j reads 8 codes of token row tau(hi, j >> 1), columns 16 (g & 1)
+  //     + 8 (j & 1) .. + 7 of the 32-column block, and after the transpose
+  //     holds column (lane & 31) of the block for the 8 tokens tau(hi, 0..7),
+  //     tau(hi, t) = 4 hi + t + 4 (t >> 2): exactly the token order of the
+  //     lane's probabilities.  Step (mb, kk) adds 1024 mb + 256 kk.
+  const int f8_kbase = 16 * (lane & 31) + 8 * hi;
+  int f8_vbase;
+  {
+    const int g16 = lane >> 4, j16 = lane & 15, t = j16 >> 1;
+    const int tau = 4 * (g16 >> 1) + t + 4 * (t >> 2);
+    f8_vbase = 512 * (g16 & 1) + 16 * tau + 8 * (j16 & 1) + 1024 * (cg * MB);
+  }
   // Source offset inside a sub-tile of this lane's part of copy piece i:
   // the piece fills physical chunk q = 64 (wave + 4 i) + lane, which holds
   // logical chunk (q mod 72) ^ g(r) of row r = q / 72.  Recomputed per copy
@@ -238,13 +257,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     };
     // LDS byte address of the copy destination of sub-tile sub: its ring stage
     auto stage_addr = [&](int sub) -> uint32_t {
-      if constexpr (F8) return (uint32_t)(uintptr_t)smem + kBufs * kSubBytes + (sub & 1) * kF8Sub;
+      if constexpr (F8) return (uint32_t)(uintptr_t)smem + (sub & (kF8Stages - 1)) * kF8Sub;
       else return (uint32_t)(uintptr_t)smem + (sub & (kStages - 1)) * kSubBytes;
     };
-    // bf16 buffer of sub-tile t
-    auto buf_of = [&](int t) -> int {
-      if constexpr (F8) return t % 3;
-      else return t & (kStages - 1);
+    // byte offset of sub-tile t's stage in smem
+    auto stage_off = [&](int t) -> int {
+      if constexpr (F8) return (t & (kF8Stages - 1)) * kF8Sub;
+      else return (t & (kStages - 1)) * kSubBytes;
     };
     // piece i of this wave lands at stage + 1 KiB * (wave + 4 i), except the
     // FP8 pieces past the 18th, which go to the sink
@@ -258,54 +277,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
 #pragma unroll
       for (int i = 0; i < kDmaN; ++i) dma(base, sub, i);
     };
-    // FP8 chunk conversion: the 16 codes of chunk q2 (row q2 & 31, codes
-    // 16 (q2 >> 5) ..) -> the two bf16 chunks of the bf16 layout (rows past
-    // the range are zeroed afterwards by fix_partial)
+    // E4M3 codes -> bf16 (exact): word x's codes 0, 1 or 2, 3 -> two bf16, the first in the low half
     auto cv_lo = [](uint32_t x) {
       return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false));
     };
     auto cv_hi = [](uint32_t x) {
       return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true));
     };
-    auto conv_store = [&](uint8_t* dst, int q2, const uint4& x) {
-      const int r = q2 & 31, c8 = q2 >> 5;
-      const uint4 lo = make_uint4(cv_lo(x.x), cv_hi(x.x), cv_lo(x.y), cv_hi(x.y));
-      const uint4 hi4 = make_uint4(cv_lo(x.z), cv_hi(x.z), cv_lo(x.w), cv_hi(x.w));
-      *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8)) = lo;
-      *reinterpret_cast<uint4*>(dst + tile_off(r, 2 * c8 + 1)) = hi4;
-    };
-    // FP8: convert landed sub-tile sub into its bf16 buffer in one go (the
-    // first two sub-tiles of a range), then a barrier
-    auto convert = [&](int sub) {
-      if constexpr (F8) {
-        const uint8_t* src = smem + kBufs * kSubBytes + (sub & 1) * kF8Sub;
-        uint8_t* dst = smem + buf_of(sub) * kSubBytes;
-        // all reads first, then convert and store (16 codes -> two bf16 chunks)
-        constexpr int kIt = (kF8Chunks + kThreads - 1) / kThreads;  // 5
-        uint4 w[kIt];
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-          const int q2 = tid + kThreads * it;
-          w[it] = (q2 < kF8Chunks) ? *reinterpret_cast<const uint4*>(src + q2 * 16) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int it = 0; it < kIt; ++it) {
-          const int q2 = tid + kThreads * it;
-          if (q2 < kF8Chunks) conv_store(dst, q2, w[it]);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        block_sync();
-      } else {
-        (void)sub;
-      }
+    auto cvt8 = [&](const uint2& x) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, make_uint4(cv_lo(x.x), cv_hi(x.x), cv_lo(x.y), cv_hi(x.y)));
     };
     // rows of a sub-tile past the sequence end hold unspecified data: zero them
     auto fix_partial = [&](int sub) {
       const int t0 = seg.tok_begin + sub * kSub;
       if (t0 + kSub > seg.tok_end) {
-        uint8_t* buf = smem + buf_of(sub) * kSubBytes;
-        for (int q2 = (seg.tok_end - t0) * kChunks + tid; q2 < kSubChunks; q2 += kThreads)
-          *reinterpret_cast<uint4*>(buf + q2 * 16) = make_uint4(0, 0, 0, 0);
+        uint8_t* buf = smem + stage_off(sub);
+        const int nv = seg.tok_end - t0;  // rows kept
+        if constexpr (F8) {
+          // chunk c of row r at 16 (32 c + r): rows nv .. 31 of every chunk column
+          for (int z = tid; z < (kSub - nv) * (kF8Row / 16); z += kThreads) {
+            const int c = z / (kSub - nv), r = nv + z % (kSub - nv);
+            *reinterpret_cast<uint4*>(buf + 16 * (32 * c + r)) = make_uint4(0, 0, 0, 0);
+          }
+        } else {
+          for (int q2 = nv * kChunks + tid; q2 < kSubChunks; q2 += kThreads)
+            *reinterpret_cast<uint4*>(buf + q2 * 16) = make_uint4(0, 0, 0, 0);
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         block_sync();
       }
@@ -352,8 +349,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         }
       };
       if constexpr (F8) {
-        issue_or_sink(0);
-        issue_or_sink(1);
+        // sub-tiles 0 .. 6, the missing ones as sink copies: the number of
+        // copies issued after any sub-tile is then the same constant
+#pragma unroll
+        for (int s2 = 0; s2 < kF8Ahead; ++s2) issue_or_sink(s2);
       } else {
         for (int s2 = 0; s2 < min(3, n_sub); ++s2) issue(s2);
       }
@@ -369,24 +368,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       auto kload = [&](const int* kb, int ks) {
         return *reinterpret_cast<const bf16x8*>(smem + kb[ks & 3] + 128 * (ks >> 2));
       };
+      // FP8: the 8 codes of score step ks, and the stage base they are read from
+      auto kload8 = [&](int kb8, int ks) { return *reinterpret_cast<const uint2*>(smem + kb8 + 512 * ks); };
+      auto kbase8 = [&](int t) {
+        int kb8 = stage_off(t) + f8_kbase;
+        __asm__ volatile("" : "+v"(kb8));
+        return kb8;
+      };
 
       // ---- prologue: sub-tile 0 ready, its scores computed
       if constexpr (F8) {
-        // each wave converts the chunks it copied: its own wait suffices
-        vm_wait_tiles<kDmaN>(1);
-        convert(0);  // ends with a barrier
+        vm_wait<(kF8Ahead - 1) * kDmaN>();  // this wave's copies of sub-tile 0 landed
+        block_sync();
         fix_partial(0);
-        issue_or_sink(2);
-        vm_wait_tiles<kDmaN>(1);
-        if (n_sub > 1) convert(1);
-        issue_or_sink(3);
       } else {
         vm_wait_tiles<kDmaN>(min(2, n_sub - 1));
         block_sync();
         fix_partial(0);
       }
       f32x16 sc;
-      {
+      if constexpr (F8) {
+        const int kb8 = kbase8(0);
+        constexpr int kAhead = 4;
+        uint2 kop[kAhead];
+#pragma unroll
+        for (int ks = 0; ks < kAhead - 1; ++ks) kop[ks] = kload8(kb8, ks);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+          if (ks + kAhead - 1 < kKSteps) kop[(ks + kAhead - 1) % kAhead] = kload8(kb8, ks + kAhead - 1);
+          if (ks == 0) mfma_v0(sc, cvt8(kop[0]), q[0]);
+          else mfma_v(sc, cvt8(kop[ks % kAhead]), q[ks]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
         int kb[4];
         kbases(0, kb);
         constexpr int kAhead = 4;
@@ -409,11 +423,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         const bool nxt = i + 1 < n_sub;
         if (nxt) {
           if constexpr (F8) {
-            // this wave's copies of sub-tile i+2 landed (sub-tile i+3 may be in
-            // flight); its conversion writes of sub-tile i+1 are done
-            vm_wait_tiles<kDmaN>(1);
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-            block_sync();  // bf16 sub-tile i+1 complete; every wave is past PV(i-1)
+            // sub-tiles i+2 .. i+6 (real or sink copies) may still be in flight
+            vm_wait<(kF8Ahead - 2) * kDmaN>();
+            block_sync();  // sub-tile i+1 landed; every wave is past PV(i-1)
             fix_partial(i + 1);
           } else {
             vm_wait_tiles<kDmaN>(i + 2 < n_sub ? 1 : 0);
@@ -421,26 +433,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
             fix_partial(i + 1);
           }
         }
-        // Sub-tile i+3 is copied during the score loop below, one 1 KiB piece
-        // every fourth MFMA: a wave can queue only a few copies, and a burst of
-        // nine would stall it for their whole transfer.  When there is no
-        // sub-tile i+3 the copies re-read the last sub-tile (an L2 hit) into
-        // the sink, so every step issues the same code and every wait count
-        // below (vmcnt) is the same constant, the sink's copies included.
-        constexpr int kAheadCopy = F8 ? 4 : 3;  // sub-tile copied during this score loop
+        // Sub-tile i+3 (FP8: i+7) is copied during the score loop below, one
+        // 1 KiB piece every fourth (FP8: seventh) MFMA: a wave can queue only a
+        // few copies, and a burst of nine would stall it for their whole
+        // transfer.  When there is no such sub-tile the copies re-read the
+        // last sub-tile (an L2 hit) into the sink, so every step issues the
+        // same code and every wait count (vmcnt) is the same constant, the
+        // sink's copies included.  The FP8 stage of sub-tile i+7 is that of
+        // sub-tile i-1, free once every wave is past PV(i-1).
+        constexpr int kAheadCopy = F8 ? kF8Ahead : 3;  // sub-tile copied during this score loop
         const bool copy_on = i + kAheadCopy < n_sub;
         const uint8_t* copy_src = tile_src(copy_on ? i + kAheadCopy : n_sub - 1);
         const uint32_t copy_dst =
             copy_on ? stage_addr(i + kAheadCopy) + wave * 1024 : (uint32_t)(uintptr_t)sink + wave * 1024;
         const uint32_t copy_stride = copy_on ? 4096u : 0u;
-        // FP8: sub-tile i+2 is converted during this score loop (when it does
-        // not exist the stage's last sub-tile is converted into the free
-        // buffer instead, which nobody reads); chunk it of this lane is
-        // q2 = tid + 256 it, and the lanes of waves 2 and 3 have no fifth
-        // chunk: theirs is read from the stage start and written to the sink
-        const uint8_t* conv_src = smem + kBufs * kSubBytes + ((i + 2) & 1) * kF8Sub;
-        uint8_t* conv_dst = smem + buf_of(i + 2) * kSubBytes;
-        uint4 conv_x = make_uint4(0, 0, 0, 0);
         int src_next = 0;
 
         // masking of sub-tile i (rare: only where some row's last visible token falls inside)
@@ -517,34 +523,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
 
         f32x16 sn;
         if (nxt) {
-          int kb[4];
-          kbases(buf_of(i + 1), kb);
           constexpr int kAhead = kOperandAhead;
-          bf16x8 kop[kAhead];
+          int kb[4];
+          int kb8 = 0;
+          if constexpr (F8) kb8 = kbase8(i + 1);
+          else kbases((i + 1) & (kStages - 1), kb);
+          using KOp = std::conditional_t<F8, uint2, bf16x8>;
+          KOp kop[kAhead];
+          auto kld = [&](int ks) -> KOp {
+            if constexpr (F8) return kload8(kb8, ks);
+            else return kload(kb, ks);
+          };
+          auto kcv = [&](const KOp& x) -> bf16x8 {
+            if constexpr (F8) return cvt8(x);
+            else return x;
+          };
 #pragma unroll
-          for (int ks = 0; ks < kAhead - 1; ++ks) kop[ks] = kload(kb, ks);
+          for (int ks = 0; ks < kAhead - 1; ++ks) kop[ks] = kld(ks);
 #pragma unroll
           for (int ks = 0; ks < kKSteps; ++ks) {
-            if (ks + kAhead - 1 < kKSteps) kop[(ks + kAhead - 1) % kAhead] = kload(kb, ks + kAhead - 1);
-            if (ks == 0) mfma_v0(sn, kop[0], q[0]);
-            else mfma_v(sn, kop[ks % kAhead], q[ks]);
+            if (ks + kAhead - 1 < kKSteps) kop[(ks + kAhead - 1) % kAhead] = kld(ks + kAhead - 1);
+            if (ks == 0) mfma_v0(sn, kcv(kop[0]), q[0]);
+            else mfma_v(sn, kcv(kop[ks % kAhead]), q[ks]);
             if (ks < kPieces) piece(ks);
             if constexpr (F8) {
-              constexpr int kConvIt = (kF8Chunks + kThreads - 1) / kThreads;  // 5 chunks per lane
-              if (ks % 6 == 1 && ks / 6 < kConvIt) {  // read chunk ks / 6
-                const int q2 = tid + kThreads * (ks / 6);
-                conv_x = *reinterpret_cast<const uint4*>(conv_src + (q2 < kF8Chunks ? q2 : 0) * 16);
+              // five 1 KiB pieces, the source offset one MFMA ahead of its copy
+              if (ks % 7 == 1 && ks / 7 < kDmaN) {
+                src_next = dma_src(ks / 7);
+                pin(src_next);
               }
-              if (ks % 6 == 4 && ks / 6 < kConvIt) {  // convert and store it
-                const int q2 = tid + kThreads * (ks / 6);
-                const bool real = q2 < kF8Chunks;  // uniform per wave: selects, no branch
-                conv_store(real ? conv_dst : sink, real ? q2 : lane, conv_x);
-              }
-              if (ks >= kKSteps - kDmaN) {  // copies after this wave's conversion reads returned
-                const int pc = ks - (kKSteps - kDmaN);
+              if (ks % 7 == 2 && ks / 7 < kDmaN) {
+                const int pc = ks / 7;
                 const bool to_sink = wave + 4 * pc >= kF8Pieces;  // uniform: a select, not a branch
-                dma_to(copy_src, to_sink ? (uint32_t)(uintptr_t)sink + wave * 1024 : copy_dst,
-                       to_sink ? 0u : copy_stride, pc);
+                dma_at(copy_src, to_sink ? (uint32_t)(uintptr_t)sink + wave * 1024 : copy_dst,
+                       to_sink ? 0u : copy_stride, pc, src_next);
               }
             } else {
               // the source offset of a copy is computed one MFMA earlier, so
@@ -566,13 +578,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         __asm__ volatile("s_nop 4" ::: "memory");  // VALU-written pb before its MFMA reads
 
         // ---- O^T += V^T . P^T for sub-tile i over this wave's columns
-        {
+        if constexpr (F8) {
+          int vb8 = stage_off(i) + f8_vbase;
+          __asm__ volatile("" : "+v"(vb8));
+          constexpr int kSteps = 2 * MB;
+          constexpr int kAhead = kOperandAhead;
+          uint2 vop[kAhead];
+          auto vload = [&](int st) {
+            const int mb = st >> 1, kk = st & 1;
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + vb8 + 1024 * mb + 256 * kk));
+            return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+          };
+#pragma unroll
+          for (int st = 0; st < kAhead - 1; ++st) vop[st] = vload(st);
+#pragma unroll
+          for (int st = 0; st < kSteps; ++st) {
+            if (st + kAhead - 1 < kSteps) vop[(st + kAhead - 1) % kAhead] = vload(st + kAhead - 1);
+            mfma_a(o[st >> 1], cvt8(vop[st % kAhead]), pb[st & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
           int vb[2][2];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int par = 0; par < 2; ++par) {
-              vb[h][par] = buf_of(i) * kSubBytes + vbase(h, par);
+              vb[h][par] = stage_off(i) + vbase(h, par);
               __asm__ volatile("" : "+v"(vb[h][par]));
             }
           constexpr int kSteps = 2 * MB;
