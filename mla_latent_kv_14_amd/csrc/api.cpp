@@ -108,10 +108,14 @@ int decode_shape(const mla_dims& d, bool fp8, DecodeShape* out) {
       //   ov = round(1.5 + R * 3200 * 0.9 / 73728)   (7 at R = 128, 3 at R = 32)
       // An FP8 tile is half the bytes, so the same fixed cost is twice the
       // tiles (12 at R = 128) and the smallest worthwhile range doubles.
+      // The smallest range is one tile (two for FP8): it binds only when the
+      // whole batch has fewer tiles than the grid, where more workgroups
+      // finish sooner (one 4096-token sequence: 28 us against 34 us with
+      // four-tile ranges) and the merge reads the extra splits in parallel.
       const int R = d.q_len * d.num_heads;
       const int64_t tile_bytes = fp8 ? 36864 : 73728;
       out->grid = cus;
-      out->min_chunk = ((R > 32) ? 4 : 2) * (fp8 ? 2 : 1);
+      out->min_chunk = fp8 ? 2 : 1;
       const int ov = (int)(((int64_t)R * 2880 + 2 * tile_bytes) / tile_bytes);
       out->ov = ov < 1 ? 1 : ov;
       return MLA_OK;
