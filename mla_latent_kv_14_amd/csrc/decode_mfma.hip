@@ -41,11 +41,12 @@
 // Pro", Practical Deployment: the latent tolerates FP8): a 32-token sub-tile
 // is 18 KiB of contiguous codes, copied HBM -> LDS by the same copy engine
 // into a ring of eight FP8 stages (seven sub-tiles ahead, as many bytes in
-// flight as the bf16 path).  A stage holds 16-code chunk c of token row r at
-// byte 512 c + 16 r, so both operand reads are contiguous over a wave: the
-// score operand (8 codes of one row) is a ds_read_b64, and the latent-sum
-// operand (8 tokens of one column) a ds_read_b64_tr_b8, the 8-bit transpose
-// read.  Each operand is converted to bf16 in registers right before its
+// flight as the bf16 path).  A stage is 18 blocks of 1 KiB, each 16 token
+// rows x 64 bytes of codes with the 16-byte chunks of a row XOR-permuted by
+// the row, so every 1 KiB copy reads 16 contiguous 64-byte row segments and
+// neither operand read has LDS bank conflicts: the score operand (8 codes of
+// one row) is a ds_read_b64, and the latent-sum operand (8 tokens of one
+// column) a ds_read_b64_tr_b8, the 8-bit transpose read.  Each operand is converted to bf16 in registers right before its
 // MFMA (E4M3 values are exact in bf16, so the matrix products see exactly
 // the cached values and run in the same order as on a bf16 cache), and
 // nothing but the codes ever goes through LDS.  Rows past the range are
@@ -177,21 +178,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   }
   auto kbase = [&](int v) { return kbase_r[v]; };
   auto vbase = [&](int h, int par) { return vbase_r[h][par]; };
-  // FP8 stage offsets (16-code chunk c of row r at 512 c + 16 r):
+  // FP8 stage offsets: 16-code chunk c of row r lies in 1 KiB block
+  // 9 (r >> 4) + (c >> 2) (16 rows x 4 chunks), at slot 4 (r & 15) + ((c & 3)
+  // ^ ((r >> 2) & 3)) of 16 bytes (f8_off).
   //   score operand: codes 16 ks + 8 hi .. + 7 of row lane & 31 at
-  //     f8_kbase + 512 ks;
+  //     f8_kbase[ks & 3] + 1024 (ks >> 2);
   //   latent-sum operand (8-bit transpose read): in each group of 16 lanes,
   //     lane j reads 8 codes of token row tau(hi, j >> 1), columns 16 (g & 1)
-  //     + 8 (j & 1) .. + 7 of the 32-column block, and after the transpose
+  //     + 8 (j & 1) .. + 7 of 32-column block cb, and after the transpose
   //     holds column (lane & 31) of the block for the 8 tokens tau(hi, 0..7),
   //     tau(hi, t) = 4 hi + t + 4 (t >> 2): exactly the token order of the
-  //     lane's probabilities.  Step (mb, kk) adds 1024 mb + 256 kk.
-  const int f8_kbase = 16 * (lane & 31) + 8 * hi;
-  int f8_vbase;
+  //     lane's probabilities.  Block cb (parity par) of tokens 16 kk .. is
+  //     at f8_vbase[par] + 1024 (9 kk + (cb >> 1)).
+  // A wave's 16-lane quarter of either read covers 16 distinct slot columns
+  // of 4 bytes x 2, so no two of its lanes share an LDS bank.
+  int f8_kbase[4];
   {
-    const int g16 = lane >> 4, j16 = lane & 15, t = j16 >> 1;
+    const int r = lane & 31, rl = r & 15;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) f8_kbase[v] = 1024 * 9 * (r >> 4) + 16 * (4 * rl + (v ^ ((rl >> 2) & 3))) + 8 * hi;
+  }
+  int f8_vbase[2];
+  {
+    const int g16 = lane >> 4, j16 = lane & 15, t = j16 >> 1, half = g16 & 1;
     const int tau = 4 * (g16 >> 1) + t + 4 * (t >> 2);
-    f8_vbase = 512 * (g16 & 1) + 16 * tau + 8 * (j16 & 1) + 1024 * (cg * MB);
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      f8_vbase[par] = 16 * (4 * tau + ((2 * par + half) ^ ((tau >> 2) & 3))) + 8 * (j16 & 1) + 1024 * (cg * MB / 2);
   }
   // Source offset inside a sub-tile of this lane's part of copy piece i:
   // the piece fills physical chunk q = 64 (wave + 4 i) + lane, which holds
@@ -201,11 +214,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   auto dma_src = [&](int i) {
     const int q = q_lane + 256 * i;
     if constexpr (F8) {
-      // FP8 sub-tile chunk q (16 codes) is row q & 31, codes 16 (q >> 5) ..;
-      // it lands at stage + 16 q, so a lane always meets the same row.  Pieces
-      // past the 18th re-read the start of the sub-tile (into the sink).
-      const int qq = q < kF8Chunks ? q : q - kF8Chunks;
-      return (qq & 31) * kF8Row + ((qq >> 5) << 4);
+      // FP8 piece k = q >> 6 fills block k (rows 16 (k / 9) .., chunks
+      // 4 (k % 9) ..): slot lane = 4 rl + s holds chunk s ^ ((rl >> 2) & 3) of
+      // row rl, so each piece reads 16 contiguous 64-byte row segments.
+      // Pieces past the 18th re-read the first blocks (into the sink).
+      const int k0 = q >> 6, k = k0 < kF8Pieces ? k0 : k0 - kF8Pieces;
+      const int rb = k >= 9 ? 1 : 0, cgk = k - 9 * rb;
+      const int rl = lane >> 2, c = 4 * cgk + ((lane & 3) ^ ((rl >> 2) & 3));
+      return (16 * rb + rl) * kF8Row + 16 * c;
     } else {
       const int r = (q * 1821) >> 17;  // q / 72 for 0 <= q < 2304
       const int pc = q - r * kChunks;
@@ -294,10 +310,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         uint8_t* buf = smem + stage_off(sub);
         const int nv = seg.tok_end - t0;  // rows kept
         if constexpr (F8) {
-          // chunk c of row r at 16 (32 c + r): rows nv .. 31 of every chunk column
+          // rows nv .. 31 of every chunk column, at their slots
           for (int z = tid; z < (kSub - nv) * (kF8Row / 16); z += kThreads) {
-            const int c = z / (kSub - nv), r = nv + z % (kSub - nv);
-            *reinterpret_cast<uint4*>(buf + 16 * (32 * c + r)) = make_uint4(0, 0, 0, 0);
+            const int c = z / (kSub - nv), r = nv + z % (kSub - nv), rl = r & 15;
+            const int off = 1024 * (9 * (r >> 4) + (c >> 2)) + 16 * (4 * rl + ((c & 3) ^ ((rl >> 2) & 3)));
+            *reinterpret_cast<uint4*>(buf + off) = make_uint4(0, 0, 0, 0);
           }
         } else {
           for (int q2 = nv * kChunks + tid; q2 < kSubChunks; q2 += kThreads)
@@ -369,11 +386,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         return *reinterpret_cast<const bf16x8*>(smem + kb[ks & 3] + 128 * (ks >> 2));
       };
       // FP8: the 8 codes of score step ks, and the stage base they are read from
-      auto kload8 = [&](int kb8, int ks) { return *reinterpret_cast<const uint2*>(smem + kb8 + 512 * ks); };
-      auto kbase8 = [&](int t) {
-        int kb8 = stage_off(t) + f8_kbase;
-        __asm__ volatile("" : "+v"(kb8));
-        return kb8;
+      auto kload8 = [&](const int* kb8, int ks) {
+        return *reinterpret_cast<const uint2*>(smem + kb8[ks & 3] + 1024 * (ks >> 2));
+      };
+      auto kbase8 = [&](int t, int* kb8) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          kb8[v] = stage_off(t) + f8_kbase[v];
+          __asm__ volatile("" : "+v"(kb8[v]));
+        }
       };
 
       // ---- prologue: sub-tile 0 ready, its scores computed
@@ -388,7 +409,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       }
       f32x16 sc;
       if constexpr (F8) {
-        const int kb8 = kbase8(0);
+        int kb8[4];
+        kbase8(0, kb8);
         constexpr int kAhead = 4;
         uint2 kop[kAhead];
 #pragma unroll
@@ -525,13 +547,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         if (nxt) {
           constexpr int kAhead = kOperandAhead;
           int kb[4];
-          int kb8 = 0;
-          if constexpr (F8) kb8 = kbase8(i + 1);
+          if constexpr (F8) kbase8(i + 1, kb);
           else kbases((i + 1) & (kStages - 1), kb);
           using KOp = std::conditional_t<F8, uint2, bf16x8>;
           KOp kop[kAhead];
           auto kld = [&](int ks) -> KOp {
-            if constexpr (F8) return kload8(kb8, ks);
+            if constexpr (F8) return kload8(kb, ks);
             else return kload(kb, ks);
           };
           auto kcv = [&](const KOp& x) -> bf16x8 {
@@ -579,14 +600,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
 
         // ---- O^T += V^T . P^T for sub-tile i over this wave's columns
         if constexpr (F8) {
-          int vb8 = stage_off(i) + f8_vbase;
-          __asm__ volatile("" : "+v"(vb8));
+          int vb8[2];
+#pragma unroll
+          for (int par = 0; par < 2; ++par) {
+            vb8[par] = stage_off(i) + f8_vbase[par];
+            __asm__ volatile("" : "+v"(vb8[par]));
+          }
           constexpr int kSteps = 2 * MB;
           constexpr int kAhead = kOperandAhead;
           uint2 vop[kAhead];
           auto vload = [&](int st) {
             const int mb = st >> 1, kk = st & 1;
-            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + vb8 + 1024 * mb + 256 * kk));
+            const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2*)(smem + vb8[mb & 1] + 1024 * (9 * kk + (mb >> 1))));
             return make_uint2((uint32_t)v.x, (uint32_t)v.y);
           };
 #pragma unroll
