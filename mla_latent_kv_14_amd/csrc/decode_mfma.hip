@@ -665,6 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       for (int mb = 0; mb < MB; ++mb) __asm__ volatile("" : "+a"(o[mb]));
 
       if (tid == 0) red_flag = 0;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the clear lands before any wave sets the flag
       block_sync();
       if (overflow && row_ok) red_flag = 1;
       __builtin_amdgcn_s_waitcnt(0xc07f);

@@ -163,6 +163,9 @@ __global__ __launch_bounds__(kGThreads, 2) void upproject_mfma(const uint16_t* _
                        pack_bf16(acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3]));
       }
   }
+  // the staged tile is read by other waves: this wave's LDS writes must have
+  // landed before the barrier (block_sync itself does not wait for them)
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   block_sync();
 #pragma unroll
   for (int i = 0; i < (kGT * 16) / kGThreads; ++i) {  // 8 chunks of 16 B per thread
@@ -173,6 +176,130 @@ __global__ __launch_bounds__(kGThreads, 2) void upproject_mfma(const uint16_t* _
   }
 }
 
+
+// The same product on 256 x 256 output tiles: eight waves, 2 (m halves) x 4
+// (n quarters), each 128 x 64 (4 x 2 MFMA tiles of 32 x 32), one workgroup per
+// CU.  A tile's operands are 512 KiB for 67 MFLOP, half the bytes per flop of
+// the 128 x 128 tile, which is what the operand stream from L2 and the
+// last-level cache bounds.  Stage layout as above (256 rows x 64 k per
+// operand, chunk c of row r at c ^ ((r >> 1) & 7)); the output tile leaves
+// through LDS in 512-B row segments, chunk c of row r at c ^ (r & 31).
+constexpr int kHT = 256;
+constexpr int kHThreads = 512;
+constexpr int kHStage = 2 * kHT * kGK * 2;  // A + B stage bytes (64 KiB)
+
+__global__ __launch_bounds__(kHThreads, 1) void upproject_mfma256(const uint16_t* __restrict__ c_kv,
+                                                                  const uint16_t* __restrict__ w_uk,
+                                                                  const uint16_t* __restrict__ w_uv,
+                                                                  const uint16_t* __restrict__ k_rope,
+                                                                  uint16_t* __restrict__ ws, int M, int N,
+                                                                  size_t v_off, size_t r_off) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kHStage];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hi = lane >> 5, mh = wave >> 2, nq = wave & 3;
+  const int n0 = blockIdx.x * kHT, m0 = blockIdx.y * kHT, which = blockIdx.z;
+  const uint16_t* bmat = which ? w_uv : w_uk;
+  uint16_t* dmat = which ? ws + v_off : ws;
+
+  // the k^R copy: rows m0 .. m0 + 255, 128 B each, by the first column tile of the Kn GEMM
+  if (which == 0 && blockIdx.x == 0) {
+    for (int q = tid; q < kHT * (kDrP / 8); q += kHThreads) {
+      const int m = m0 + q / (kDrP / 8), c = q % (kDrP / 8);
+      if (m < M)
+        *reinterpret_cast<uint4*>(ws + r_off + (size_t)m * kDrP + 8 * c) =
+            *reinterpret_cast<const uint4*>(k_rope + (size_t)m * kDrP + 8 * c);
+    }
+  }
+
+  // Stage copy: piece i (0..3) of this wave for operand X fills physical
+  // chunks q = 512 i + 64 wave + lane of the 256 x 8-chunk tile: row q >> 3,
+  // physical chunk q & 7, logical chunk (q & 7) ^ gswz(row).
+  auto copy_stage = [&](int stage, int kc) {
+    const uint32_t base = (uint32_t)(uintptr_t)smem + stage * kHStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 512 * i + 64 * wave + lane;
+      const int r = q >> 3, lc = (q & 7) ^ gswz(r);
+      const int ma = min(m0 + r, M - 1);
+      const uint32_t off_a = (uint32_t)(((size_t)ma * kDcP + kc * kGK + 8 * lc) * 2);
+      const uint32_t off_b = (uint32_t)(((size_t)(n0 + r) * kDcP + kc * kGK + 8 * lc) * 2);
+      const uint32_t da = __builtin_amdgcn_readfirstlane(base + 1024 * (8 * i + wave));
+      const uint32_t db = __builtin_amdgcn_readfirstlane(base + kHT * kGK * 2 + 1024 * (8 * i + wave));
+      __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off_a), "s"(c_kv), "{m0}"(da) : "memory");
+      __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off_b), "s"(bmat), "{m0}"(db) : "memory");
+    }
+  };
+
+  f32x16 acc[2][4];  // [n tile][m tile]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+
+  const int r32 = lane & 31;
+  auto opnd = [&](int stage, int rowoff, int row, int ks) {
+    const int c = (2 * ks + hi) ^ gswz(row);
+    return *reinterpret_cast<const bf16x8*>(smem + stage * kHStage + rowoff + 16 * c);
+  };
+
+  constexpr int kChunksK = kDcP / kGK;  // 8
+  copy_stage(0, 0);
+  for (int kc = 0; kc < kChunksK; ++kc) {
+    vm_wait<0>();
+    block_sync();  // stage kc & 1 landed everywhere; stage (kc + 1) & 1 no longer read
+    if (kc + 1 < kChunksK) copy_stage((kc + 1) & 1, kc + 1);
+    const int st = kc & 1;
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      bf16x8 av[4], bv[2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ra = 128 * mh + 32 * t + r32;
+        av[t] = opnd(st, ra * kGK * 2, ra, ks);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rb = 64 * nq + 32 * t + r32;
+        bv[t] = opnd(st, kHT * kGK * 2 + rb * kGK * 2, rb, ks);
+      }
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[tn], av[tm], acc[tn][tm], 0, 0, 0);
+    }
+  }
+
+  // lane (m = lane & 31, hi) holds, in acc[tn][tm], columns 8 (r >> 2) + 4 hi
+  // + (r & 3) of the 32-column tile tn of its wave
+  block_sync();  // every wave is done with the operand stages
+  uint8_t* ot = smem;  // [256 rows][512 B]
+#pragma unroll
+  for (int tm = 0; tm < 4; ++tm) {
+    const int r = 128 * mh + 32 * tm + r32;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 64 * nq + 32 * tn + 8 * g + 4 * hi;  // 4 columns = 8 B
+        const int c = col >> 3, half = (col >> 2) & 1;
+        *reinterpret_cast<uint2*>(ot + r * 512 + ((c ^ (r & 31)) << 4) + 8 * half) =
+            make_uint2(pack_bf16(acc[tn][tm][4 * g], acc[tn][tm][4 * g + 1]),
+                       pack_bf16(acc[tn][tm][4 * g + 2], acc[tn][tm][4 * g + 3]));
+      }
+  }
+  // the staged tile is read by other waves: this wave's LDS writes must have
+  // landed before the barrier (block_sync itself does not wait for them)
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  block_sync();
+#pragma unroll
+  for (int i = 0; i < (kHT * 32) / kHThreads; ++i) {  // 16 chunks of 16 B per thread
+    const int q = i * kHThreads + tid, r = q >> 5, c = q & 31, m = m0 + r;
+    if (m < M)
+      *reinterpret_cast<uint4*>(dmat + (size_t)m * N + n0 + 8 * c) =
+          *reinterpret_cast<const uint4*>(ot + r * 512 + ((c ^ (r & 31)) << 4));
+  }
+}
 
 // ------------------------------------------------------------------ attention
 // LDS key row (640 B = 40 chunks): Kn (chunks 0-15) | V (16-31) | k^R (32-39),
@@ -507,6 +634,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_mfma(PrefillArgs a) {
     for (int mb = 0; mb < kAMB; ++mb) __asm__ volatile("" : "+a"(o[mb]));
 
     if (tid == 0) red_flag = 0;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the clear lands before any wave sets the flag
     block_sync();
     if (overflow && row_ok) red_flag = 1;
     __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -646,10 +774,16 @@ hipError_t launch_prefill(const mla_dims& d, int tokens, int max_seqlen, const i
   const PrefillLayout Lw = prefill_layout(d, tokens);
   if (mfma) {
     const int N = d.num_heads * kDnP;
-    hipLaunchKernelGGL(upproject_mfma, dim3(N / kGT, (tokens + kGT - 1) / kGT, 2), dim3(kGThreads), 0, stream,
-                       static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(w_uk),
-                       static_cast<const uint16_t*>(w_uv), static_cast<const uint16_t*>(k_rope),
-                       static_cast<uint16_t*>(ws), tokens, N, (size_t)Lw.v_off, (size_t)Lw.r_off);
+    if (N % kHT == 0)  // an even head count: the 256 x 256 tiles
+      hipLaunchKernelGGL(upproject_mfma256, dim3(N / kHT, (tokens + kHT - 1) / kHT, 2), dim3(kHThreads), 0, stream,
+                         static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(w_uk),
+                         static_cast<const uint16_t*>(w_uv), static_cast<const uint16_t*>(k_rope),
+                         static_cast<uint16_t*>(ws), tokens, N, (size_t)Lw.v_off, (size_t)Lw.r_off);
+    else
+      hipLaunchKernelGGL(upproject_mfma, dim3(N / kGT, (tokens + kGT - 1) / kGT, 2), dim3(kGThreads), 0, stream,
+                         static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(w_uk),
+                         static_cast<const uint16_t*>(w_uv), static_cast<const uint16_t*>(k_rope),
+                         static_cast<uint16_t*>(ws), tokens, N, (size_t)Lw.v_off, (size_t)Lw.r_off);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     PrefillArgs a{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),

@@ -151,3 +151,27 @@ def test_prefill_full_mixed():
 
 def test_prefill_full_mixed_noncausal():
     _sampled("prefill_mixed_bf16", n_tok=12, causal=False)
+
+
+# ------------------------------------------------------------------ repeatability
+
+@pytest.mark.parametrize("name,heads", [("prefill_4x4k_bf16", 128), ("prefill_mixed_bf16", 5)])
+def test_prefill_repeatable(name, heads):
+    """Three calls on the same inputs give the same bits: the up-projected workspace, u and lse.  H = 128
+    runs the 256 x 256 up-projection tiles, H = 5 (an odd head count) the 128 x 128 ones.  (Both once
+    staged their output tile in LDS and let other waves read it without waiting for the writes to land,
+    which made a few 16-byte pieces of the workspace differ from call to call.)"""
+    prob = make_prefill_problem(workload(name, heads=heads))
+    r = PrefillRunner(prob)
+    outs = []
+    for _ in range(3):
+        r.workspace.zero_()
+        r.u.zero_()
+        r.lse.zero_()
+        r.prefill()
+        torch.cuda.synchronize()
+        outs.append((r.workspace.clone(), r.u.clone(), r.lse.clone()))
+    for k in (1, 2):
+        nws = int((outs[k][0] != outs[0][0]).sum())
+        say(f"  {name} H={heads}: call {k}: {nws} workspace words differ")
+        assert nws == 0 and torch.equal(outs[k][1], outs[0][1]) and torch.equal(outs[k][2], outs[0][2])
