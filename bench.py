@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Decode-step benchmark for libmla on one MI355X.
 
-A step is one pass of the whole hot path over one batch: plan, absorb_q,
-split-KV attention, then the log-sum-exp combine and absorb_out (one fused
-call), for every sequence of the workload.  Inputs are seeded synthetic
+A step is one pass of the whole hot path over one batch: absorb_q with the
+split-KV plan (one launch), the split-KV attention, then the log-sum-exp
+combine and absorb_out (one fused call), for every sequence of the workload.  Inputs are seeded synthetic
 tensors already resident in HBM.
 
 Timing is cold: before every timed step (or call) a flush kernel reads
@@ -287,7 +287,7 @@ def measure_decode(prob, timer, K, warmup, peaks, cold_only=False, traffic=None,
 
     wl = prob.wl
     r = DecodeRunner(prob, device="cuda:0")
-    calls = [("plan", r.plan), ("absorb_q", r.absorb_q), ("decode", r.decode_planned),
+    calls = [("absorb_q_plan", r.absorb_q_plan), ("decode", r.decode_planned),
              ("combine_absorb_out", r.combine_absorb_out)]
 
     def step():

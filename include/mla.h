@@ -177,6 +177,22 @@ int mla_decode_noalloc(const mla_dims* dims, const void* q_cat, const void* kv_c
 int mla_decode_plan(const mla_dims* dims, const int32_t* seq_lens, int32_t num_splits, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* mla_absorb_q and mla_decode_plan in one launch: the same q_cat and the same
+ * schedule in the workspace, bit for bit, with the planner running as one
+ * more workgroup of the absorb_q kernel (both depend only on their own
+ * inputs), so a decode step is three launches: this, mla_decode_planned and
+ * mla_combine_absorb_out.  Arguments and errors as for the two calls; every
+ * argument of both is validated before anything is enqueued.  Where the
+ * absorb_q matrix-core kernel does not serve the dims, the two kernels are
+ * enqueued one after the other.  The _fp8 form plans for mla_decode_fp8's
+ * kernels (mla_decode_planned_fp8). */
+int mla_absorb_q_plan(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk, void* q_cat,
+                      const int32_t* seq_lens, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int mla_absorb_q_plan_fp8(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* w_uk,
+                          void* q_cat, const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 /* Second half of mla_decode: enqueue only the attention kernel, reading the
  * schedule (and the lengths) that mla_decode_plan left in the workspace.
  * Arguments as for mla_decode; num_splits must equal the planned value. */

@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     D = ctypes.POINTER(mla_dims)
     sig = {
         "mla_absorb_q": [D, P, P, P, P, P],
+        "mla_absorb_q_plan": [D, P, P, P, P, P, I32, P, SZ, P],
+        "mla_absorb_q_plan_fp8": [D, P, P, P, P, P, I32, P, SZ, P],
         "mla_decode_num_splits": [D, I32, I64, ctypes.POINTER(I32)],
         "mla_choose_splits": [D, P, I32, ctypes.POINTER(I32)],
         "mla_choose_splits_fp8": [D, P, I32, ctypes.POINTER(I32)],
@@ -149,6 +151,29 @@ def mla_absorb_q(dims, q_nope, q_rope, w_uk, q_cat, stream=None):
         ctypes.byref(d), _ptr(q_nope, "q_nope", st, rows * d.d_nope), _ptr(q_rope, "q_rope", st, rows * d.d_rope),
         _ptr(w_uk, "w_uk", st, d.num_heads * d.d_nope * d.d_c),
         _ptr(q_cat, "q_cat", st, rows * (d.d_c + d.d_rope)), _stream(stream)))
+
+
+def _absorb_q_plan(fn, dims, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace, stream):
+    d, st = dims, _storage_dtype(dims)
+    rows = d.batch * d.q_len * d.num_heads
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    _check(fn, getattr(load(), fn)(
+        ctypes.byref(d), _ptr(q_nope, "q_nope", st, rows * d.d_nope), _ptr(q_rope, "q_rope", st, rows * d.d_rope),
+        _ptr(w_uk, "w_uk", st, d.num_heads * d.d_nope * d.d_c), _ptr(q_cat, "q_cat", st, rows * (d.d_c + d.d_rope)),
+        _ptr(seq_lens, "seq_lens", torch.int32, d.batch), int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_absorb_q_plan(dims, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace, stream=None):
+    """mla_absorb_q and mla_decode_plan in one launch."""
+    _absorb_q_plan("mla_absorb_q_plan", dims, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace, stream)
+
+
+def mla_absorb_q_plan_fp8(dims, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace, stream=None):
+    """mla_absorb_q and mla_decode_plan_fp8 in one launch."""
+    _absorb_q_plan("mla_absorb_q_plan_fp8", dims, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace,
+                   stream)
 
 
 def mla_decode_num_splits(dims, max_seq_len: int, total_tokens: int) -> int:

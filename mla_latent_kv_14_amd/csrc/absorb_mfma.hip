@@ -13,6 +13,7 @@
 //   both halves are multiplied, which keeps about 16 mantissa bits of o.
 #include "common.h"
 #include "internal.h"
+#include "plan_body.h"
 
 namespace mla {
 namespace {
@@ -38,10 +39,19 @@ constexpr int kNQ = 128;   // absorb_q: columns of q~ per workgroup
 // and stores them as one 8-byte write.
 constexpr int kRowsQ = 64;  // rows of q_nope per workgroup (two 32-row MFMA tiles)
 
+// With a plan (launched with one more x slice), workgroup (H, 0, 0) runs the
+// decode planner (plan_body.h) on the lengths instead, so the step's schedule
+// costs no launch of its own; the rest of that slice does nothing.
 __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
-                                                          uint16_t* __restrict__ q_cat, int M, int H, int d_r) {
+                                                          uint16_t* __restrict__ q_cat, int M, int H, int d_r,
+                                                          PlanArgs pa) {
+  if ((int)blockIdx.x == H) {
+    __shared__ PlanShared psh;
+    if (blockIdx.y == 0 && blockIdx.z == 0) plan_body(pa, psh);
+    return;
+  }
   // W quarter: row k (0..127) holds 16 chunks of 16 B; chunk c sits at c ^ (4 * (k & 3))
   __shared__ __attribute__((aligned(16))) uint8_t wt[kDN * kNQ * 2];
   const int h = blockIdx.x, nq = blockIdx.y, mbase = blockIdx.z * kRowsQ;
@@ -352,11 +362,13 @@ bool absorb_mfma_supported(const mla_dims& d) {
 }
 
 hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
-                                void* q_cat, hipStream_t stream) {
+                                void* q_cat, hipStream_t stream, const PlanArgs* plan) {
   const int M = d.batch * d.q_len;
-  hipLaunchKernelGGL(absorb_q_mfma, dim3(d.num_heads, kDC / kNQ, (M + kRowsQ - 1) / kRowsQ), dim3(kThreads), 0, stream,
-                     (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk, (uint16_t*)q_cat, M,
-                     d.num_heads, d.d_rope);
+  PlanArgs pa{};
+  if (plan != nullptr) pa = *plan;
+  hipLaunchKernelGGL(absorb_q_mfma, dim3(d.num_heads + (plan != nullptr ? 1 : 0), kDC / kNQ, (M + kRowsQ - 1) / kRowsQ),
+                     dim3(kThreads), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
+                     (uint16_t*)q_cat, M, d.num_heads, d.d_rope, pa);
   return hipGetLastError();
 }
 

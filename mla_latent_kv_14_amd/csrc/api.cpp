@@ -11,6 +11,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "plan_body.h"
 #include "mla.h"
 
 namespace {
@@ -337,6 +338,48 @@ int mla_choose_splits(const mla_dims* d, const int32_t* seq_lens_host, int32_t m
 int mla_choose_splits_fp8(const mla_dims* d, const int32_t* seq_lens_host, int32_t max_seq_len,
                           int32_t* num_splits) {
   return choose_splits_impl(d, seq_lens_host, max_seq_len, num_splits, true);
+}
+
+namespace {
+
+static int absorb_q_plan_impl(const mla_dims* d, const void* q_nope, const void* q_rope, const void* w_uk, void* q_cat,
+                       const int32_t* seq_lens, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                       void* stream, bool fp8) {
+  int st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(q_nope) || !ptr_ok(w_uk) || !ptr_ok(q_cat) || (d->d_rope > 0 && !ptr_ok(q_rope)))
+    return MLA_ERR_INVALID_ARG;
+  st = check_decode_common(d, num_splits, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  if (!ptr_ok(seq_lens)) return MLA_ERR_INVALID_ARG;
+  DecodeShape sh;
+  st = decode_shape(*d, fp8, &sh);
+  if (st != MLA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (!force_generic() && mla::absorb_mfma_supported(*d)) {
+    const mla::PlanArgs pa =
+        mla::make_plan_args(*d, seq_lens, num_splits, sh.grid, sh.min_chunk, sh.ov, static_cast<int32_t*>(workspace));
+    return to_status(mla::launch_absorb_q_mfma(*d, q_nope, q_rope, w_uk, q_cat, s, &pa));
+  }
+  hipError_t e = mla::launch_absorb_q_generic(*d, q_nope, q_rope, w_uk, q_cat, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  return to_status(enqueue_plan(*d, seq_lens, num_splits, workspace, sh, s));
+}
+
+}  // namespace
+
+int mla_absorb_q_plan(const mla_dims* d, const void* q_nope, const void* q_rope, const void* w_uk, void* q_cat,
+                      const int32_t* seq_lens, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return absorb_q_plan_impl(d, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace, workspace_bytes, stream,
+                            false);
+}
+
+int mla_absorb_q_plan_fp8(const mla_dims* d, const void* q_nope, const void* q_rope, const void* w_uk, void* q_cat,
+                          const int32_t* seq_lens, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return absorb_q_plan_impl(d, q_nope, q_rope, w_uk, q_cat, seq_lens, num_splits, workspace, workspace_bytes, stream,
+                            true);
 }
 
 int mla_decode_plan(const mla_dims* d, const int32_t* seq_lens, int32_t num_splits, void* workspace,

@@ -33,8 +33,10 @@ hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* 
 
 // matrix-core absorption GEMMs for bf16, d_nope = d_v = 128, d_c = 512 (absorb_mfma.hip)
 bool absorb_mfma_supported(const mla_dims& d);
+struct PlanArgs;  // plan_body.h
+// plan: when given, one extra workgroup of the same launch runs the decode planner
 hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
-                                void* q_cat, hipStream_t stream);
+                                void* q_cat, hipStream_t stream, const PlanArgs* plan = nullptr);
 hipError_t launch_absorb_out_mfma(const mla_dims& d, const float* o, const void* w_uv, void* out,
                                   hipStream_t stream);
 // fused log-sum-exp merge + W_UV product (same support as the MFMA absorb

@@ -108,10 +108,16 @@ class DecodeRunner:
                                       self.o if (keep_latent or not fused) else None,
                                       self.lse if (keep_latent or not fused) else None, stream)
 
+    def absorb_q_plan(self, stream=None):
+        """absorb_q and the plan in one launch (the planner runs as one more workgroup)."""
+        fn = libmla.mla_absorb_q_plan_fp8 if self.fp8 else libmla.mla_absorb_q_plan
+        fn(self.dims, self.q_nope, self.q_rope, self.w_uk, self.q_cat, self.seq_lens, self.num_splits,
+           self.workspace, stream)
+
     def fused_step(self, stream=None):
-        """One decode step as the bench runs it: plan, absorb_q, attention, fused merge + W_UV."""
-        self.plan(stream)
-        self.absorb_q(stream)
+        """One decode step as the bench runs it: absorb_q with the plan, attention, fused merge + W_UV
+        (three launches)."""
+        self.absorb_q_plan(stream)
         self.decode_planned(stream)
         self.combine_absorb_out(stream=stream)
 
@@ -120,7 +126,7 @@ class DecodeRunner:
         (torch.cuda.CUDAGraph) and return it.
 
         The libmla calls enqueue kernels only (no memsets, no allocation), so
-        the graph holds exactly the four kernels of each step."""
+        the graph holds exactly the three kernels of each step."""
         side = torch.cuda.Stream(device=self.device)
         side.wait_stream(torch.cuda.current_stream(self.device))
         with torch.cuda.stream(side):

@@ -391,3 +391,28 @@ def test_decode_noalloc_host_checks():
         assert call(d, **over) == libmla.MLA_ERR_INVALID_ARG
     assert call(_dims(batch=65537)) == libmla.MLA_ERR_WORKSPACE
     assert call(_dims(dtype=9)) == libmla.MLA_ERR_UNSUPPORTED
+
+
+def _absorb_q_plan(d, fn="mla_absorb_q_plan", **over):
+    args = dict(q_nope=P(FAKE), q_rope=P(FAKE), w_uk=P(FAKE), q_cat=P(FAKE), lens=P(FAKE), splits=4, ws=P(FAKE),
+                ws_bytes=1 << 20)
+    args.update(over)
+    return _call(fn, ctypes.byref(d), args["q_nope"], args["q_rope"], args["w_uk"], args["q_cat"], args["lens"],
+                 args["splits"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("fn", ["mla_absorb_q_plan", "mla_absorb_q_plan_fp8"])
+@pytest.mark.parametrize("over", [
+    {"q_nope": None}, {"w_uk": None}, {"q_cat": None}, {"lens": None}, {"ws": None}, {"q_cat": P(FAKE + 4)},
+    {"splits": 0}, {"splits": 5000},
+])
+def test_absorb_q_plan_invalid_args(fn, over):
+    """Every argument of both halves is checked before anything is enqueued (no GPU is touched here)."""
+    assert _absorb_q_plan(_dims(), fn, **over) == libmla.MLA_ERR_INVALID_ARG
+
+
+def test_absorb_q_plan_workspace_too_small():
+    d = _dims()
+    need = libmla.mla_decode_workspace_bytes(d, 4)
+    assert _absorb_q_plan(d, ws_bytes=need - 4) == libmla.MLA_ERR_WORKSPACE
+    assert _absorb_q_plan(d, "mla_absorb_q_plan_fp8", ws_bytes=8) == libmla.MLA_ERR_WORKSPACE

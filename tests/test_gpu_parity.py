@@ -397,3 +397,39 @@ def test_choose_splits_equals_num_splits():
     big[3], big[4] = 1 << 30, -5  # clamped into [0, MB * block_size]
     clamp = np.clip(big.astype(np.int64), 0, 128 * 64)
     assert libmla.mla_choose_splits(bf, big) == libmla.mla_decode_num_splits(bf, int(clamp.max()), int(clamp.sum()))
+
+
+@pytest.mark.parametrize("name,over", [
+    ("single_4k_bf16", dict(batch=5, lengths=("fixed", (1, 70, 640, 3000, 129)))),
+    ("mtp2_lognormal_bf16", dict(batch=6, lengths=("fixed", (2, 64, 65, 66, 129, 700)))),
+    ("single_4k_fp8", dict(batch=3, lengths=("fixed", (5, 900, 4096)))),
+    ("tiny_f32", {}),
+])
+def test_absorb_q_plan_equals_two_calls(name, over):
+    """mla_absorb_q_plan (the planner as one more workgroup of the absorb_q launch) writes the same q_cat and
+    the same schedule as mla_absorb_q followed by mla_decode_plan, bit for bit; float32 storage takes the
+    portable two-launch route through the same entry point."""
+    p = make_problem(workload(name, **over), 71)
+    r = DecodeRunner(p)
+    outs = []
+    for fused in (False, True):
+        r.workspace.fill_(-7)
+        r.q_cat.zero_()
+        if fused:
+            r.absorb_q_plan()
+        else:
+            r.plan()
+            r.absorb_q()
+        torch.cuda.synchronize()
+        outs.append((r.workspace.clone(), r.q_cat.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]), "schedule differs"
+    assert torch.equal(outs[0][1].view(torch.int16) if outs[0][1].dtype == torch.bfloat16 else outs[0][1],
+                       outs[1][1].view(torch.int16) if outs[1][1].dtype == torch.bfloat16 else outs[1][1])
+    r.decode_planned()
+    r.combine_absorb_out()
+    torch.cuda.synchronize()
+    u1 = r.u.clone()
+    r.u.zero_()
+    r.fused_step()
+    torch.cuda.synchronize()
+    assert torch.equal(r.u, u1)
