@@ -1,4 +1,4 @@
-"""Device-resident buffers for one decode problem plus the four-call step.
+"""Device-resident buffers for one decode problem plus the three-launch step.
 
 Allocation and upload use torch (device memory only); every step of the
 computation is a libmla call.
