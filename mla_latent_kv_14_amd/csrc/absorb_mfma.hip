@@ -271,53 +271,78 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
   __shared__ float4 gsum[32][8][16];  // [row group][column block][thread of the row], 64 KiB
   const int h = blockIdx.x, m0 = blockIdx.y * 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  WuvOperands op;
-  wuv_request(w_uv, h, wave, lane, op);
 
   const int rows = min(32, M - m0);
   const int lgP = merge_groups_log2(rows), P = 1 << lgP;
-  const int g = tid >> 4, j = tid & 15;  // row group g = (row r, block lane p)
+  const int g = tid >> 4, j = tid & 15, j8 = j & 7;  // row group g = (row r, block lane p)
   const int r = g >> lgP, p = g & (P - 1), m = m0 + r;
   const bool valid = r < rows;
+
+  // Loads complete in issue order, so the row's first split lse values are
+  // requested before anything else: waiting for them (and for the first
+  // chunk of partials) never waits for the W_UV rows, which are requested
+  // after that chunk and are needed only by the product.
+  const float* lp = lse_part + ((size_t)(valid ? m : m0) * H + h) * S;
+  const float lfirst = (valid && j8 < S) ? lp[j8] : -INFINITY;
+  float total = -INFINITY;
+  if (valid) {
+    total = split_lse_first(lfirst, lp, S, j8);
+    if (lse_out != nullptr && p == 0 && j == 0) lse_out[(size_t)m * H + h] = total;
+  }
 
   float4 acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (valid) {
-    const float* lp = lse_part + ((size_t)m * H + h) * S;
-    const float total = split_lse(lp, S, j & 7);
-    if (lse_out != nullptr && p == 0 && j == 0) lse_out[(size_t)m * H + h] = total;
-    // bf16 partials: four columns (8 bytes) per load
-    const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)m * H + h) * S * kDC) + j;
-    auto fma4 = [&](float wgt, const uint2* x) {
+  // bf16 partials: four columns (8 bytes) per load
+  const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)(valid ? m : m0) * H + h) * S * kDC) + j;
+  auto fma4 = [&](float wgt, const uint2* x) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[k].x = fmaf(wgt, __uint_as_float(x[k].x << 16), acc[k].x);
-        acc[k].y = fmaf(wgt, __uint_as_float(x[k].x & 0xffff0000u), acc[k].y);
-        acc[k].z = fmaf(wgt, __uint_as_float(x[k].y << 16), acc[k].z);
-        acc[k].w = fmaf(wgt, __uint_as_float(x[k].y & 0xffff0000u), acc[k].w);
+    for (int k = 0; k < 8; ++k) {
+      acc[k].x = fmaf(wgt, __uint_as_float(x[k].x << 16), acc[k].x);
+      acc[k].y = fmaf(wgt, __uint_as_float(x[k].x & 0xffff0000u), acc[k].y);
+      acc[k].z = fmaf(wgt, __uint_as_float(x[k].y << 16), acc[k].z);
+      acc[k].w = fmaf(wgt, __uint_as_float(x[k].y & 0xffff0000u), acc[k].w);
+    }
+  };
+  // The group's splits in merge order, four at a time: chunk c covers splits
+  // s0 .. s0 + 3 of block p + P (c >> 1), s0 = 8 (p + P (c >> 1)) + 4 (c & 1).
+  // Splits of block 0 take their lse from the lanes that loaded it; splits
+  // with lse_s = -inf are skipped (their o_s is never read).
+  auto chunk_start = [&](int c) { return kMergeBlock * (p + P * (c >> 1)) + 4 * (c & 1); };
+  auto load_chunk = [&](int s0, float* wv, uint2 (*x)[8]) {
+    float ls[4];
+    if (s0 < kMergeBlock) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ls[u] = __shfl(lfirst, (lane & ~7) | (s0 + u), 64);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ls[u] = (s0 + u < S) ? lp[s0 + u] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wv[u] = (s0 + u >= S || ls[u] == -INFINITY) ? 0.f : expf(ls[u] - total);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (wv[u] != 0.f) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[u][k] = src[(size_t)(s0 + u) * (kDC / 4) + 16 * k];
       }
-    };
-    for (int blk = p; blk * kMergeBlock < S; blk += P) {
-      const int s_end = min(S, (blk + 1) * kMergeBlock);
-      for (int s0 = blk * kMergeBlock; s0 < s_end; s0 += 4) {
-        float wv[4];
-        uint2 x[4][8];
+  };
+  auto merge_chunk = [&](const float* wv, uint2 (*x)[8]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float ls = (s0 + u < s_end) ? lp[s0 + u] : -INFINITY;
-          wv[u] = (ls == -INFINITY) ? 0.f : expf(ls - total);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (wv[u] != 0.f) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) x[u][k] = src[(size_t)(s0 + u) * (kDC / 4) + 16 * k];
-          }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (wv[u] != 0.f) fma4(wv[u], x[u]);
-      }
+    for (int u = 0; u < 4; ++u)
+      if (wv[u] != 0.f) fma4(wv[u], x[u]);
+  };
+  float wv[4];
+  uint2 x[4][8];
+  const bool first_chunk = valid && chunk_start(0) < S;
+  if (first_chunk) load_chunk(chunk_start(0), wv, x);
+  WuvOperands op;
+  wuv_request(w_uv, h, wave, lane, op);
+  if (first_chunk) {
+    merge_chunk(wv, x);
+    for (int c = 1; chunk_start(c) < S; ++c) {
+      load_chunk(chunk_start(c), wv, x);
+      merge_chunk(wv, x);
     }
   }
   // float4 column block k of thread j is columns 4 (j + 16 k) .. + 3

@@ -103,17 +103,24 @@ __host__ __device__ __forceinline__ int merge_groups_log2(int rows) {
   return lg;
 }
 
-__device__ __forceinline__ float split_lse(const float* lp, int S, int j) {
-  float mx = -INFINITY;
-  for (int s = j; s < S; s += 8) mx = fmaxf(mx, lp[s]);
+// log sum_s exp(lp[s]) over the S splits of one row, by 8 lanes (lane j of
+// the 8 takes s = j, j + 8, ...); `first` is the lane's lp[j] (-inf if j >= S),
+// loaded by the caller, so that the first load can be issued ahead of others.
+__device__ __forceinline__ float split_lse_first(float first, const float* lp, int S, int j) {
+  float mx = fmaxf(-INFINITY, first);
+  for (int s = j + 8; s < S; s += 8) mx = fmaxf(mx, lp[s]);
 #pragma unroll
   for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   if (mx == -INFINITY) return -INFINITY;
   float z = 0.f;
-  for (int s = j; s < S; s += 8) z += expf(lp[s] - mx);
+  if (j < S) z += expf(first - mx);
+  for (int s = j + 8; s < S; s += 8) z += expf(lp[s] - mx);
 #pragma unroll
   for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off, 64);
   return mx + logf(z);
+}
+__device__ __forceinline__ float split_lse(const float* lp, int S, int j) {
+  return split_lse_first(j < S ? lp[j] : -INFINITY, lp, S, j);
 }
 
 // ---- schedule lookups shared by every decode kernel ----------------------------------
