@@ -117,7 +117,8 @@ int mla_choose_splits_fp8(const mla_dims* dims, const int32_t* seq_lens_host, in
                           int32_t* num_splits);
 
 /* Bytes of device workspace mla_decode needs (the work schedule it computes
- * on the device: a few words plus one int32 per sequence). */
+ * on the device: a few words plus two int32 per scheduled sequence, counting
+ * the head groups described at mla_decode, so up to four per sequence). */
 int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t* bytes);
 
 /* Split-KV attention over the paged latent cache (the guide's section 4,
@@ -147,7 +148,14 @@ int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t*
  * Equivalent to mla_decode_plan followed by mla_decode_planned (two kernels:
  * a one-workgroup planner that turns seq_lens into a token-balanced schedule
  * in the workspace, then the attention kernel).  Each sequence's tokens are
- * divided into at most S contiguous ranges.  Unused cache slots may hold
+ * divided into at most S contiguous ranges.  Head groups: with q_len = 1 and
+ * 64 or 128 heads, when B * ceil(MB * block_size / 64) 64-token tiles at most
+ * would leave most CUs idle, the heads of each sequence are split into 2 or 4
+ * groups of 32 (the largest count whose grouped tile total still fits the
+ * CUs), and each group is scheduled as a sequence of its own, divided into
+ * at most S ranges; the outputs' layout and meaning do not change.  The
+ * grouping depends only on dims and the device, so mla_decode_plan and
+ * mla_decode_planned always agree on it.  Unused cache slots may hold
  * anything (NaN included): they never reach a result.  A length outside
  * [0, MB * block_size] is clamped into it for memory safety (the result for
  * that sequence is then meaningless). */

@@ -45,6 +45,12 @@ struct DecodeArgs {
   float scale;
   int32_t B, Lq, H, d_c, d_rope, block_size, max_blocks, num_blocks, splits;
   float kv_scale;  // FP8 cache: a stored code stands for kv_scale * its value (1 otherwise)
+  // Head groups: with q_len = 1 the heads of a sequence may be split into
+  // 2^hg_log2 groups, each scheduled as a sequence of its own (B, H above
+  // then count groups and heads per group; q_cat and the partial results
+  // keep their layout).  Group b reads the block table of sequence
+  // b >> hg_log2.
+  int32_t hg_log2;
 };
 
 // ---- float <-> storage conversions -------------------------------------------------

@@ -140,6 +140,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   const int hi = lane >> 5;
   const int S = a.splits;
   const int32_t* len = ws + kWsHeader + a.B + 1;
+  // a schedule planned for another batch (or head grouping) is never walked
+  if (ws[6] != a.B) return;
 
   if (blockIdx.x == 0) mark_empty_sequences(a, tid, blockDim.x);
 
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   auto table_window = [&](const Segment& s) -> int {
     const int j0 = s.tok_begin / a.block_size;
     const int nblk = (s.tok_end - 1) / a.block_size - j0 + 1;
-    return table[(size_t)s.b * a.max_blocks + j0 + min(lane, nblk - 1)];
+    return table[(size_t)(s.b >> a.hg_log2) * a.max_blocks + j0 + min(lane, nblk - 1)];
   };
   Segment seg, nseg;
   bool have = walk.next(seg);
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     const int b = seg.b;
     const int L = len[b];
     const int n_sub = (seg.tok_end - seg.tok_begin + kSub - 1) / kSub;
-    const int32_t* trow = table + (size_t)b * a.max_blocks;
+    const int32_t* trow = table + (size_t)(b >> a.hg_log2) * a.max_blocks;
     const int j0 = seg.tok_begin / a.block_size;
 
     // Copy of one sub-tile: the source row address (uniform) and this wave's
@@ -716,9 +718,9 @@ bool decode_mfma_supported(const mla_dims& d) {
 
 hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
                               const int32_t* ws, float scale, int splits, int grid, void* o_part, float* lse_part,
-                              hipStream_t stream, bool fp8, float kv_scale) {
+                              hipStream_t stream, bool fp8, float kv_scale, int hg_log2) {
   DecodeArgs a{q_cat, cache, table, ws, o_part, lse_part, scale, d.batch, d.q_len, d.num_heads, d.d_c, d.d_rope,
-               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale};
+               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale, hg_log2};
   const int R = d.q_len * d.num_heads;
   const uint16_t* qc = static_cast<const uint16_t*>(q_cat);
   const uint8_t* kv = static_cast<const uint8_t*>(cache);

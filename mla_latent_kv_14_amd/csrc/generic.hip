@@ -110,6 +110,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
   const C* cache = (const C*)a.cache;
   const float kv = kF8 ? a.kv_scale : 1.f;
   const int32_t* len = a.ws + kWsHeader + a.B + 1;
+  // a schedule planned for another batch (or head grouping) is never walked
+  if (a.ws[6] != a.B) return;
 
   if (blockIdx.x == 0 && blockIdx.y == 0) mark_empty_sequences(a, threadIdx.x, blockDim.x);
   SegmentWalker walk;
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
       size_t off = 0;
       float s = -INFINITY;
       if (valid) {
-        int blk = a.block_table[(size_t)b * a.max_blocks + t / a.block_size];
+        int blk = a.block_table[(size_t)(b >> a.hg_log2) * a.max_blocks + t / a.block_size];
         blk = min(max(blk, 0), a.num_blocks - 1);
         off = ((size_t)blk * a.block_size + t % a.block_size) * D;
         float dot = 0.f;
@@ -286,7 +288,7 @@ hipError_t launch_decode_generic(const mla_dims& d, const void* q_cat, const voi
                                  const int32_t* ws, float scale, int splits, int grid, void* o_part,
                                  float* lse_part, hipStream_t stream, bool fp8, float kv_scale) {
   DecodeArgs a{q_cat, cache, table, ws, o_part, lse_part, scale, d.batch, d.q_len, d.num_heads, d.d_c, d.d_rope,
-               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale};
+               d.block_size, d.max_blocks_per_seq, d.num_blocks, splits, kv_scale, 0};
   const int R = d.q_len * d.num_heads;
   dim3 g(grid, (R + kThreads / 64 - 1) / (kThreads / 64));
   if (d.dtype == MLA_F32) {

@@ -9,8 +9,9 @@
 namespace mla {
 
 // planner (plan.hip)
+// d counts head groups as sequences when hg_log2 > 0 (plan_body.h)
 hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk, int ov,
-                       int32_t* ws, hipStream_t stream);
+                       int32_t* ws, hipStream_t stream, int hg_log2);
 
 // portable kernels for any supported shape (generic.hip)
 hipError_t launch_absorb_q_generic(const mla_dims& d, const void* q_nope, const void* q_rope, const void* w_uk,
@@ -27,9 +28,10 @@ hipError_t launch_absorb_out_generic(const mla_dims& d, const float* o, const vo
 // matrix-core decode for bf16, d_c = 512, d_rope = 64 (decode_mfma.hip)
 bool decode_mfma_supported(const mla_dims& d);
 // fp8: the cache holds E4M3 codes standing for kv_scale times their value
+// hg_log2 > 0: d counts head groups as sequences (DecodeArgs::hg_log2)
 hipError_t launch_decode_mfma(const mla_dims& d, const void* q_cat, const void* cache, const int32_t* table,
                               const int32_t* ws, float scale, int splits, int grid, void* o_part, float* lse_part,
-                              hipStream_t stream, bool fp8, float kv_scale);
+                              hipStream_t stream, bool fp8, float kv_scale, int hg_log2);
 
 // matrix-core absorption GEMMs for bf16, d_nope = d_v = 128, d_c = 512 (absorb_mfma.hip)
 bool absorb_mfma_supported(const mla_dims& d);

@@ -15,9 +15,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs pa) {
 }  // namespace
 
 hipError_t launch_plan(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk, int ov,
-                       int32_t* ws, hipStream_t stream) {
+                       int32_t* ws, hipStream_t stream, int hg_log2) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream,
-                     make_plan_args(d, seq_lens, splits, grid, min_chunk, ov, ws));
+                     make_plan_args(d, seq_lens, splits, grid, min_chunk, ov, ws, hg_log2));
   return hipGetLastError();
 }
 

@@ -19,15 +19,18 @@ namespace mla {
 
 constexpr int kPlanThreads = 256;
 
+// With head groups (hg_log2 > 0), d counts groups: B = batch << hg_log2
+// scheduled sequences, entry b taking the length of sequence b >> hg_log2.
 struct PlanArgs {
   const int32_t* seq_lens;
   int32_t* ws;
-  int B, q_len, max_len, splits, grid, min_chunk, ov;
+  int B, q_len, max_len, splits, grid, min_chunk, ov, hg_log2;
 };
 
 inline PlanArgs make_plan_args(const mla_dims& d, const int32_t* seq_lens, int splits, int grid, int min_chunk,
-                               int ov, int32_t* ws) {
-  return PlanArgs{seq_lens, ws, d.batch, d.q_len, d.max_blocks_per_seq * d.block_size, splits, grid, min_chunk, ov};
+                               int ov, int32_t* ws, int hg_log2) {
+  return PlanArgs{seq_lens, ws,  d.batch, d.q_len, d.max_blocks_per_seq * d.block_size, splits, grid, min_chunk, ov,
+                  hg_log2};
 }
 
 struct PlanShared {
@@ -70,8 +73,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
 
   int local_sum = 0, local_max = 0, local_empty = 0;
   for (int b = threadIdx.x; b < B; b += kPlanThreads) {
-    int L = pa.seq_lens[b];
-    if (L < pa.q_len || L > pa.max_len) atomicMin(&sh.bad, b);
+    int L = pa.seq_lens[b >> pa.hg_log2];
+    if (L < pa.q_len || L > pa.max_len) atomicMin(&sh.bad, b >> pa.hg_log2);
     L = min(max(L, 0), pa.max_len);
     len[b] = L;
     const int n = (L + kPlanTile - 1) / kPlanTile;
@@ -124,7 +127,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
     ws[6] = B;
     ws[7] = empty;
     ws[8] = pa.ov;
-    for (int k = 9; k < kWsHeader; ++k) ws[k] = 0;
+    ws[9] = pa.hg_log2;
+    for (int k = 10; k < kWsHeader; ++k) ws[k] = 0;
   }
 }
 

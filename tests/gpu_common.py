@@ -74,13 +74,17 @@ WS_HEADER = 16
 def replay_schedule(ws: np.ndarray):
     """Host replay of the planner's schedule read back from the workspace.
 
-    Header words: chunk, groups, total, maxn, splits, error, B, empty, ov.
-    Sequence b occupies [cu[b], cu[b+1]) of the schedule line: ov overhead
+    Header words: chunk, groups, total, maxn, splits, error, B, empty, ov,
+    hg_log2.  With head groups (hg = 2^hg_log2 > 1, q_len = 1 only) the
+    schedule's B counts (sequence, head group) pairs: entry e is group
+    e % hg of sequence e // hg and covers heads [g H / hg, (g + 1) H / hg).
+    Entry e occupies [cu[e], cu[e+1]) of the schedule line: ov overhead
     tiles (none for an empty sequence), then its real tiles.  Workgroup w
     owns line tiles [w*chunk, (w+1)*chunk).
-    Returns (header dict, list of segments (w, b, tok_begin, tok_end, split, nsplits), lengths).
+    Returns (header dict with the batch B and the group count hg, list of
+    segments (w, b, tok_begin, tok_end, split, nsplits, g), lengths per sequence).
     """
-    chunk, groups, total, maxn, splits, err, B, empty, ov = (int(x) for x in ws[:9])
+    chunk, groups, total, maxn, splits, err, B, empty, ov, hgl = (int(x) for x in ws[:10])
     cu = ws[WS_HEADER:WS_HEADER + B + 1].astype(np.int64)
     lens = ws[WS_HEADER + B + 1:WS_HEADER + 2 * B + 1].astype(np.int64)
     segs = []
@@ -95,10 +99,11 @@ def replay_schedule(ws: np.ndarray):
                 if lo >= hi:
                     continue
                 first = rs // chunk
-                segs.append((w, b, int((lo - rs) * PLAN_TILE), int(min((hi - rs) * PLAN_TILE, lens[b])),
-                             int(w - first), int((cu[b + 1] - 1) // chunk - first + 1)))
+                segs.append((w, b >> hgl, int((lo - rs) * PLAN_TILE), int(min((hi - rs) * PLAN_TILE, lens[b])),
+                             int(w - first), int((cu[b + 1] - 1) // chunk - first + 1), b & ((1 << hgl) - 1)))
     else:
         for b in range(B):
-            segs.append((b % groups, b, 0, int(lens[b]), 0, 1))
-    hdr = dict(chunk=chunk, groups=groups, total=total, maxn=maxn, splits=splits, error=err, B=B, empty=empty, ov=ov)
-    return hdr, segs, lens
+            segs.append((b % groups, b >> hgl, 0, int(lens[b]), 0, 1, b & ((1 << hgl) - 1)))
+    hdr = dict(chunk=chunk, groups=groups, total=total, maxn=maxn, splits=splits, error=err, B=B >> hgl,
+               empty=empty, ov=ov, hg=1 << hgl)
+    return hdr, segs, lens[::1 << hgl]

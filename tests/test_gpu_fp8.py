@@ -123,21 +123,23 @@ def test_fp8_partials_against_oracle():
     cache = _values(p)
     o_part, lse_part = to64(r.o_partial), to64(r.lse_partial)
     H, d_c = wl.heads, wl.d_c
+    Hg = H // hdr["hg"]  # head groups each hold their own pieces
     seen = set()
-    for (_, b, t0, t1, s, ns) in segs:
+    for (_, b, t0, t1, s, ns, g) in segs:
         L = int(p.seq_lens[b])
+        hs = slice(g * Hg, (g + 1) * Hg)
         rows = orc.gather_rows(cache, p.block_table, b, L)[t0:t1]
-        vis = np.ones((H, t1 - t0), dtype=bool)
-        o_ref, l_ref = orc.latent_attention_partial_reference(q_cat[b].reshape(H, -1), rows, p.scale, d_c, vis)
-        got_l = lse_part[b, :, :, s].reshape(-1)
-        got_o = o_part[b, :, :, s].reshape(H, d_c)
+        vis = np.ones((Hg, t1 - t0), dtype=bool)
+        o_ref, l_ref = orc.latent_attention_partial_reference(q_cat[b].reshape(H, -1)[hs], rows, p.scale, d_c, vis)
+        got_l = lse_part[b, :, :, s].reshape(-1)[hs]
+        got_o = o_part[b, :, :, s].reshape(H, d_c)[hs]
         assert np.abs(got_l - l_ref).max() <= 2e-2
         assert np.abs(got_o - o_ref).max() <= 2e-2
         _, rel = metrics(got_o, o_ref)
         assert rel <= 1e-2
         seen.add((b, s))
         for s2 in range(ns, r.num_splits):
-            assert np.isneginf(lse_part[b, :, :, s2]).all()
+            assert np.isneginf(lse_part[b, :, :, s2].reshape(-1)[hs]).all()
     assert {b for b, _ in seen} == set(range(wl.batch))
 
 

@@ -108,14 +108,15 @@ def test_split_sweep(splits):
     r = _full_check(make_problem(wl, 21), num_splits=splits, check_intermediate=False)
     hdr, segs, _ = replay_schedule(r.workspace.cpu().numpy())
     per_seq = {}
-    for (_, b, t0, t1, s, ns) in segs:
-        per_seq.setdefault(b, []).append((t0, t1, s, ns))
+    for (_, b, t0, t1, s, ns, g) in segs:
+        per_seq.setdefault((b, g), []).append((t0, t1, s, ns))
     for b, L in enumerate(r.prob.seq_lens):
-        pieces = sorted(per_seq[b])
-        assert pieces[0][0] == 0 and pieces[-1][1] == L
-        assert all(p[1] == q[0] for p, q in zip(pieces, pieces[1:]))  # contiguous, no overlap
-        assert [p[2] for p in pieces] == list(range(len(pieces)))
-        assert len(pieces) == pieces[0][3] <= r.num_splits
+        for g in range(hdr["hg"]):  # each head group covers the sequence on its own
+            pieces = sorted(per_seq[(b, g)])
+            assert pieces[0][0] == 0 and pieces[-1][1] == L
+            assert all(p[1] == q[0] for p, q in zip(pieces, pieces[1:]))  # contiguous, no overlap
+            assert [p[2] for p in pieces] == list(range(len(pieces)))
+            assert len(pieces) == pieces[0][3] <= r.num_splits
 
 
 def test_block_permutation_bit_identical():
@@ -319,16 +320,19 @@ def test_decode_partials_against_oracle(name, lens):
     cache = p.cache.float().numpy()
     o_part, lse_part = to64(r.o_partial), to64(r.lse_partial)
     Lq, H, d_c = wl.q_len, wl.heads, wl.d_c
+    Hg = H // hdr["hg"]  # head groups (q_len = 1 only) each hold their own pieces
     seen = set()
-    for (_, b, t0, t1, s, ns) in segs:
+    for (_, b, t0, t1, s, ns, g) in segs:
         L = int(p.seq_lens[b])
+        sel = np.arange(Lq * H) if hdr["hg"] == 1 else np.arange(g * Hg, (g + 1) * Hg)
         rows = orc.gather_rows(cache, p.block_table, b, L)[t0:t1]
         vis = np.zeros((Lq * H, t1 - t0), dtype=bool)
         for j in range(Lq):
             vis[j * H:(j + 1) * H] = (np.arange(t0, t1) <= L - Lq + j)[None, :]
-        o_ref, l_ref = orc.latent_attention_partial_reference(q_cat[b].reshape(Lq * H, -1), rows, p.scale, d_c, vis)
-        got_l = lse_part[b, :, :, s].reshape(-1)
-        got_o = o_part[b, :, :, s].reshape(Lq * H, d_c)
+        o_ref, l_ref = orc.latent_attention_partial_reference(q_cat[b].reshape(Lq * H, -1)[sel], rows, p.scale, d_c,
+                                                              vis[sel])
+        got_l = lse_part[b, :, :, s].reshape(-1)[sel]
+        got_o = o_part[b, :, :, s].reshape(Lq * H, d_c)[sel]
         fin = np.isfinite(l_ref)
         assert np.array_equal(np.isfinite(got_l), fin)
         tol = 1e-5 if wl.dtype == "f32" else 2e-2
@@ -339,7 +343,7 @@ def test_decode_partials_against_oracle(name, lens):
             assert rel <= (1e-6 if wl.dtype == "f32" else 1e-2)
         seen.add((b, s))
         for s2 in range(ns, r.num_splits):  # unused splits are marked empty
-            assert np.isneginf(lse_part[b, :, :, s2]).all()
+            assert np.isneginf(lse_part[b, :, :, s2].reshape(-1)[sel]).all()
     assert {b for b, _ in seen} == set(range(wl.batch))
 
 
@@ -399,10 +403,40 @@ def test_choose_splits_equals_num_splits():
     assert libmla.mla_choose_splits(bf, big) == libmla.mla_decode_num_splits(bf, int(clamp.max()), int(clamp.sum()))
 
 
+@pytest.mark.parametrize("batch,heads,q_len,max_len", [(1, 128, 1, 4096), (2, 128, 1, 4096), (3, 128, 1, 2100),
+                                                        (4, 128, 1, 4096), (1, 64, 1, 4096), (5, 64, 1, 4096),
+                                                        (1, 16, 2, 4096), (16, 128, 1, 8192)])
+def test_head_groups(batch, heads, q_len, max_len):
+    """With q_len = 1 and 64 or 128 heads, a batch whose largest possible tile count (B x max_blocks x
+    block_size / 64) fits the CUs twice or four times over is scheduled in groups of 32 heads: the schedule
+    header records the grouping, every (sequence, group) pair covers its sequence once, and u matches the
+    oracle in every element."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wl = workload("single_4k_bf16", batch=batch, heads=heads, q_len=q_len,
+                  lengths=("fixed", tuple(max_len - 97 * i for i in range(batch))))
+    p = make_problem(wl, 83)
+    max_tiles = batch * -(-p.max_blocks * wl.block_size // 64)
+    expect = 0
+    if q_len == 1 and heads in (64, 128):
+        while expect < (2 if heads == 128 else 1) and (max_tiles << (expect + 1)) <= cus:
+            expect += 1
+    r = _full_check(p, check_intermediate=False)
+    hdr, segs, lens = replay_schedule(r.workspace.cpu().numpy())
+    say(f"  {cus} CUs, at most {max_tiles} tiles: {hdr['hg']} head groups, splits={r.num_splits}")
+    assert hdr["hg"] == 1 << expect and hdr["B"] == batch and hdr["error"] == 0
+    assert np.array_equal(lens, p.seq_lens)
+    covered = {}
+    for (_, b, t0, t1, _, _, g) in segs:
+        covered[(b, g)] = covered.get((b, g), 0) + (t1 - t0)
+    assert covered == {(b, g): int(p.seq_lens[b]) for b in range(batch) for g in range(hdr["hg"])}
+
+
 @pytest.mark.parametrize("name,over", [
     ("single_4k_bf16", dict(batch=5, lengths=("fixed", (1, 70, 640, 3000, 129)))),
+    ("single_4k_bf16", dict(batch=1, lengths=("fixed", (3000,)))),  # four head groups
     ("mtp2_lognormal_bf16", dict(batch=6, lengths=("fixed", (2, 64, 65, 66, 129, 700)))),
     ("single_4k_fp8", dict(batch=3, lengths=("fixed", (5, 900, 4096)))),
+    ("single_4k_fp8", dict(batch=2, lengths=("fixed", (900, 2500)))),  # two head groups
     ("tiny_f32", {}),
 ])
 def test_absorb_q_plan_equals_two_calls(name, over):

@@ -16,10 +16,11 @@ The planted key has k^R = 32 q^R of the chosen row at d_rope = 64 (128 q^R
 at d_rope = 16; a power of two, so it is exact in bf16), which adds about
 2000 to that raw score.  The
 chosen row then attends almost only to the planted key, so its output is
-W^UV c of that key: entries of order one, compared to the same tolerances as
-every other case (bf16: max-abs 2e-2 and relative L2 1e-2; float32 max-abs
-1e-5), except the prefill's u, whose element bar adds 2^-7 |u| for the two
-bf16 roundings of order-one outputs.  Every element of u and lse is
+W^UV c of that key: entries of order one (several units), compared to the
+same tolerances as every other case (bf16: max-abs 2e-2 and relative L2
+1e-2; float32 max-abs 1e-5), except that the bf16 element bar on u adds
+2^-7 |u| for the two bf16 roundings such outputs go through (the decode's
+split partial and u; the prefill's V and u).  Every element of u and lse is
 compared.
 """
 from __future__ import annotations
@@ -88,16 +89,18 @@ def _decode_oracle(prob):
 def _check_planted_past_first_tile(ws, plants, lens):
     """Token 40 and the last token lie at least one key tile into the piece of the schedule that holds them
     (the middle plant may or may not; either way the result must be exact)."""
-    _, segs, _ = replay_schedule(ws)
+    hdr, segs, _ = replay_schedule(ws)
     past = 0
     for (b, t, _, _) in plants:
-        owners = [(t0, t1) for (_, bb, t0, t1, _, _) in segs if bb == b and t0 <= t < t1]
-        assert len(owners) == 1, (b, t, owners)
-        if t - owners[0][0] >= SUB:
-            past += 1
-        else:
-            assert t not in (40, int(lens[b]) - 1), f"planted token {t} of sequence {b} is in its piece's first tile"
-    say(f"  {past} of {len(plants)} planted keys lie past the first tile of their piece")
+        owners = [(t0, t1) for (_, bb, t0, t1, _, _, _) in segs if bb == b and t0 <= t < t1]
+        assert len(owners) == hdr["hg"], (b, t, owners)  # one piece per head group
+        for (t0, _) in owners:
+            if t - t0 >= SUB:
+                past += 1
+            else:
+                assert t not in (40, int(lens[b]) - 1), f"planted token {t} of sequence {b} is in its piece's first tile"
+    say(f"  {past} of {len(plants) * hdr['hg']} (planted key, head group) pairs lie past the first tile of "
+        f"their piece")
 
 
 def _check_lse(gpu, ref, dtype):
@@ -127,7 +130,7 @@ def _decode_case(wl, seed, num_splits=None):
     q = prob.f64("q_rope")
     for (b, t, j, h) in plants:
         assert (GAMMA_NUM / wl.d_rope) * float(q[b, j, h] @ q[b, j, h]) * prob.scale * np.log2(np.e) > 140
-    assert_parity(to64(r.u), u, wl.dtype, "u")
+    _check_decode_u(to64(r.u), u, wl.dtype, "u")
     _check_lse(to64(r.lse), lse, wl.dtype)
     mo, ro = metrics(to64(r.o), o)
     say(f"  o: max_abs={mo:.3e} rel_l2={ro:.3e}")
@@ -135,7 +138,25 @@ def _decode_case(wl, seed, num_splits=None):
     r.u.fill_(0)
     r.combine_absorb_out()  # the fused merge + W_UV route over the same partials
     torch.cuda.synchronize()
-    assert_parity(to64(r.u), u, wl.dtype, "u (fused merge)")
+    _check_decode_u(to64(r.u), u, wl.dtype, "u (fused merge)")
+
+
+def _check_decode_u(got, u, dtype, what):
+    """A planted row attends to one key and returns W^UV c of that key: entries of order one (several units),
+    where the bf16 path rounds twice, the split's partial o_s and u itself, half a step (2^-9 relative) each.
+    As for the prefill below, the bf16 bar per element is the workloads' 2e-2 plus 2^-7 |u| for those two
+    roundings (a factor 2 of margin), with relative L2 1e-2 over the whole output; float32 keeps 1e-5."""
+    if dtype == "f32":
+        assert_parity(got, u, dtype, what)
+        return
+    max_abs, rel = metrics(got, u)
+    say(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e} max|u|={np.abs(u).max():.2f}")
+    assert np.isfinite(got).all() and rel <= 1e-2
+    over = np.abs(got - u) - (2e-2 + 2.0 ** -7 * np.abs(u))
+    if (over > 0).any():
+        idx = tuple(int(x) for x in np.unravel_index(np.argmax(over), over.shape))
+        say(f"  worst element {idx}: gpu {got[idx]:.5f} oracle {u[idx]:.5f}; {int((over > 0).sum())} over")
+    assert (over <= 0).all()
 
 
 LENS = (700, 2100, 300)  # (L - 1) mod 64 >= 32 for each
