@@ -152,29 +152,44 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
 
 // ------------------------------------------------------------ W_UV product
 // u tile (32 rows x 128 outputs) = o tile (32 x 512, LDS bf16 hi + lo, row r's
-// 16-B chunk c at c ^ (r & 15)) . W_UV[h]^T, by 8 waves: wave w computes
-// outputs 32 (w & 3) .. + 31 over d_c half (w >> 2) with the W_UV rows it
-// requested into bw; the second half adds into the first through LDS.  Both
-// kernels that apply W_UV use this, so they round identically.
+// 16-B chunk c at c ^ (r & 15)) . W_UV[h]^T.  Output block vblk (32 outputs)
+// over d_c half chalf is one wave's MFMA chain, with the W_UV rows it
+// requested into bw; the second half adds into the first through LDS.  With
+// all 128 outputs in one workgroup, wave w takes block w & 3 and half w >> 2;
+// a workgroup with half the outputs (z of 2) gives blocks 2 z, 2 z + 1 to
+// waves w & 1 with (w & 2) == 0, and the others idle through the product.
+// Every output element takes the same chain either way, and both kernels
+// that apply W_UV use this, so they round identically.
 constexpr int kThreadsC = 512;
 
 struct WuvOperands {
   uint4 bw[kDC / 32];
 };
 
-__device__ __forceinline__ void wuv_request(const uint16_t* __restrict__ w_uv, int h, int wave, int lane,
+struct WuvRole {
+  int vblk, chalf;
+  bool active;
+};
+__device__ __forceinline__ WuvRole wuv_role(int wave, int nz, int z) {
+  if (nz == 1) return WuvRole{wave & 3, wave >> 2, true};
+  return WuvRole{2 * z + (wave & 1), wave >> 2, (wave & 2) == 0};
+}
+
+__device__ __forceinline__ void wuv_request(const uint16_t* __restrict__ w_uv, int h, const WuvRole& ro, int lane,
                                             WuvOperands& op) {
-  const int v = 32 * (wave & 3) + (lane & 31), hi = lane >> 5;
-  const uint16_t* wrow = w_uv + ((size_t)h * kDV + v) * kDC + (wave >> 2) * (kDC / 2) + 8 * hi;
+  if (!ro.active) return;
+  const int v = 32 * ro.vblk + (lane & 31), hi = lane >> 5;
+  const uint16_t* wrow = w_uv + ((size_t)h * kDV + v) * kDC + ro.chalf * (kDC / 2) + 8 * hi;
 #pragma unroll
   for (int ks = 0; ks < kDC / 32; ++ks) op.bw[ks] = *reinterpret_cast<const uint4*>(wrow + 16 * ks);
 }
 
 __device__ __forceinline__ void wuv_product(const uint8_t (*ot)[32 * kDC * 2], float (*red)[16][64],
-                                            const WuvOperands& op, int wave, int lane, int m0, int M, int H, int h,
-                                            uint16_t* __restrict__ out) {
-  const int vblk = wave & 3, chalf = wave >> 2, hi = lane >> 5, r = lane & 31;
+                                            const WuvOperands& op, const WuvRole& ro, int lane, int m0, int M, int H,
+                                            int h, uint16_t* __restrict__ out) {
+  const int vblk = ro.vblk, chalf = ro.chalf, hi = lane >> 5, r = lane & 31;
   f32x16 acc = f32x16{};
+  if (ro.active) {
 #pragma unroll
   for (int kq = 0; kq < kDC / 32; ++kq) {
     const int ks = chalf * (kDC / 32) + kq;
@@ -185,12 +200,13 @@ __device__ __forceinline__ void wuv_product(const uint8_t (*ot)[32 * kDC * 2], f
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
   }
-  if (chalf == 1) {
+  }
+  if (ro.active && chalf == 1) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) red[vblk][rr][lane] = acc[rr];
   }
   __syncthreads();
-  if (chalf == 0) {
+  if (ro.active && chalf == 0) {
     const int v = 32 * vblk + r;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -230,7 +246,8 @@ __global__ __launch_bounds__(kThreadsC) void absorb_out_mfma(const float* __rest
   const int h = blockIdx.x, m0 = blockIdx.y * 32;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   WuvOperands op;
-  wuv_request(w_uv, h, wave, lane, op);
+  const WuvRole ro = wuv_role(wave, 1, 0);
+  wuv_request(w_uv, h, ro, lane, op);
   // thread (row r, lane j of 16) stages float4 columns j + 16 k, k < 8
   {
     const int r = tid >> 4, j = tid & 15, m = m0 + r;
@@ -243,7 +260,7 @@ __global__ __launch_bounds__(kThreadsC) void absorb_out_mfma(const float* __rest
     for (int k = 0; k < 8; ++k) stage_hilo(ot, r, (j + 16 * k) >> 1, (j + 16 * k) & 1, x[k]);
   }
   __syncthreads();
-  wuv_product(ot, red, op, wave, lane, m0, M, H, h, out);
+  wuv_product(ot, red, op, ro, lane, m0, M, H, h, out);
 }
 
 // ------------------------------------------------------------ combine + absorb_out
@@ -287,7 +304,7 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
   float total = -INFINITY;
   if (valid) {
     total = split_lse_first(lfirst, lp, S, j8);
-    if (lse_out != nullptr && p == 0 && j == 0) lse_out[(size_t)m * H + h] = total;
+    if (lse_out != nullptr && p == 0 && j == 0 && blockIdx.z == 0) lse_out[(size_t)m * H + h] = total;
   }
 
   float4 acc[8];
@@ -337,7 +354,8 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
   const bool first_chunk = valid && chunk_start(0) < S;
   if (first_chunk) load_chunk(chunk_start(0), wv, x);
   WuvOperands op;
-  wuv_request(w_uv, h, wave, lane, op);
+  const WuvRole ro = wuv_role(wave, (int)gridDim.z, (int)blockIdx.z);
+  wuv_request(w_uv, h, ro, lane, op);
   if (first_chunk) {
     merge_chunk(wv, x);
     for (int c = 1; chunk_start(c) < S; ++c) {
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
   }
   // float4 column block k of thread j is columns 4 (j + 16 k) .. + 3
   auto finish = [&](int k, const float4& v) {
-    if (valid && o_latent != nullptr)
+    if (valid && o_latent != nullptr && blockIdx.z == 0)
       reinterpret_cast<float4*>(o_latent + ((size_t)m * H + h) * kDC)[j + 16 * k] = v;
     stage_hilo(ot, r, (j + 16 * k) >> 1, (j + 16 * k) & 1, v);
   };
@@ -377,7 +395,7 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
         stage_hilo(ot, rz, (j + 16 * k) >> 1, (j + 16 * k) & 1, make_float4(0.f, 0.f, 0.f, 0.f));
   }
   __syncthreads();
-  wuv_product(ot, red, op, wave, lane, m0, M, H, h, out);
+  wuv_product(ot, red, op, ro, lane, m0, M, H, h, out);
 }
 
 }  // namespace
@@ -398,9 +416,14 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const voi
 }
 
 hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const void* o_part, const float* lse_part,
-                                   const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream) {
+                                   const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream,
+                                   int cus) {
   const int M = d.batch * d.q_len;
-  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32), dim3(kThreadsC), 0, stream,
+  // a grid that fills at most half the CUs splits each tile's 128 outputs
+  // over two workgroups (both merge the tile; each reads half of W_UV[h])
+  const int tiles = d.num_heads * ((M + 31) / 32);
+  const int nz = (2 * tiles <= cus) ? 2 : 1;
+  hipLaunchKernelGGL(combine_out_mfma, dim3(d.num_heads, (M + 31) / 32, nz), dim3(kThreadsC), 0, stream,
                      static_cast<const uint16_t*>(o_part), lse_part,
                      (const uint16_t*)w_uv, (uint16_t*)out, o_latent, lse, M, d.num_heads, splits);
   return hipGetLastError();

@@ -516,8 +516,13 @@ int mla_combine_absorb_out(const mla_dims* d, int32_t num_splits, const void* o_
     return MLA_ERR_INVALID_ARG;
   if (num_splits < 1 || num_splits > kMaxSplits) return MLA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (!force_generic() && mla::absorb_mfma_supported(*d))
-    return to_status(mla::launch_combine_out_mfma(*d, num_splits, o_partial, lse_partial, w_uv, out, o_latent, lse, s));
+  if (!force_generic() && mla::absorb_mfma_supported(*d)) {
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != MLA_OK) return st;
+    return to_status(
+        mla::launch_combine_out_mfma(*d, num_splits, o_partial, lse_partial, w_uv, out, o_latent, lse, s, cus));
+  }
   // two-kernel route: the merged latent output goes through o_latent
   if (o_latent == nullptr) return MLA_ERR_UNSUPPORTED;
   hipError_t e = mla::launch_combine(*d, num_splits, o_partial, lse_partial, o_latent, lse, s);

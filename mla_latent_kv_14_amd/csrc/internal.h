@@ -43,8 +43,10 @@ hipError_t launch_absorb_out_mfma(const mla_dims& d, const float* o, const void*
                                   hipStream_t stream);
 // fused log-sum-exp merge + W_UV product (same support as the MFMA absorb
 // kernels, any split count)
+// cus: the device's CU count (a grid of at most half of it splits the outputs over two workgroups)
 hipError_t launch_combine_out_mfma(const mla_dims& d, int splits, const void* o_part, const float* lse_part,
-                                   const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream);
+                                   const void* w_uv, void* out, float* o_latent, float* lse, hipStream_t stream,
+                                   int cus);
 
 // cache append (append.hip): matrix-core split-K path for bf16 storage with
 // d_model % 128 == 0 and (d_c + d_rope) % 32 == 0, portable path otherwise
