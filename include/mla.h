@@ -117,8 +117,9 @@ int mla_choose_splits_fp8(const mla_dims* dims, const int32_t* seq_lens_host, in
                           int32_t* num_splits);
 
 /* Bytes of device workspace mla_decode needs (the work schedule it computes
- * on the device: a few words plus two int32 per scheduled sequence, counting
- * the head groups described at mla_decode, so up to four per sequence). */
+ * on the device: a header, four int32 per workgroup for up to 1024
+ * workgroups (16 KiB), and two int32 per scheduled sequence, counting the
+ * head groups described at mla_decode, so up to four per sequence). */
 int mla_decode_workspace_bytes(const mla_dims* dims, int32_t num_splits, size_t* bytes);
 
 /* Split-KV attention over the paged latent cache (the guide's section 4,

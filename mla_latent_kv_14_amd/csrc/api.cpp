@@ -168,7 +168,7 @@ int decode_shape(const mla_dims& d, bool fp8, DecodeShape* out) {
 // hipGetSymbolAddress, with that device current, and only that address is
 // handed to the kernels.
 constexpr int kScratchMaxBatch = 65536;
-constexpr size_t kScratchWords = (size_t)mla::kWsHeader + 2 * (size_t)kScratchMaxBatch + 1;
+constexpr size_t kScratchWords = (size_t)mla::kWsCu + 2 * (size_t)kScratchMaxBatch + 1;
 static __device__ __align__(256) int32_t scratch[kScratchWords];
 
 // Device address of this device's scratch (nullptr and MLA_ERR_HIP on failure).

@@ -23,9 +23,15 @@ constexpr int kPlanTile = 64;
 //   [6] batch   B
 //   [7] empty   number of sequences with no tokens
 //   [8] ov      overhead tiles charged at the start of every non-empty sequence
-//   [9 .. 15]   reserved (0)
-//   [16 .. 16+B]      cu: start of each sequence on the schedule line (B + 1 words)
-//   [17+B .. 17+2B)   len: per-sequence length, clamped to [0, MB * block_size]
+//   [9] hg_log2 head groups (the schedule's B counts groups, see DecodeArgs)
+//   [10 .. 15]  reserved (0)
+//   [16 .. 16+4F)     first: for workgroup w < F = kFirstMax (chunked mode), the
+//                     sequence of its first segment and that sequence's cu[b],
+//                     cu[b+1] and len[b], so that a workgroup starts without
+//                     searching cu (one round of loads instead of log2 B + 2)
+//   [C .. C+B]        cu: start of each sequence on the schedule line (B + 1
+//                     words), C = kWsCu = 16 + 4F
+//   [C+B+1 .. C+2B+1) len: per-sequence length, clamped to [0, MB * block_size]
 // On the schedule line sequence b occupies [cu[b], cu[b+1]): first ov
 // overhead tiles that hold no tokens (they stand for the fixed cost of
 // starting a piece of a sequence: loading its queries, writing its partial
@@ -33,7 +39,9 @@ constexpr int kPlanTile = 64;
 // nothing.  Workgroup w owns the line range [w*chunk, (w+1)*chunk), so that
 // cost rather than token count is balanced across workgroups.
 constexpr int kWsHeader = 16;
-inline size_t workspace_words(int batch) { return (size_t)kWsHeader + 2 * (size_t)batch + 1; }
+constexpr int kFirstMax = 1024;
+constexpr int kWsCu = kWsHeader + 4 * kFirstMax;
+inline size_t workspace_words(int batch) { return (size_t)kWsCu + 2 * (size_t)batch + 1; }
 
 struct DecodeArgs {
   const void* q_cat;
@@ -157,19 +165,40 @@ struct SegmentWalker {
   int b;         // current sequence
   int t_begin;   // workgroup's first line tile, t_end its end (chunked mode)
   int t_end;
+  int pre_b, pre_c0, pre_c1, pre_len;  // the planner's first segment: b, cu[b], cu[b + 1], len[b]
 
   __device__ __forceinline__ void init(const int32_t* ws_, int w_) {
     ws = ws_;
     w = w_;
+    // the first-segment words sit at a fixed offset, so they are requested
+    // together with the header words rather than after them
+    const bool has_first = w < kFirstMax;
+    int f0 = 0, f1 = 0, f2 = 0, f3 = 0;
+    if (has_first) {
+      const int32_t* f = ws + kWsHeader + 4 * w;
+      f0 = f[0];
+      f1 = f[1];
+      f2 = f[2];
+      f3 = f[3];
+    }
     chunk = ws[0];
     groups = ws[1];
     total = ws[2];
     B = ws[6];
     ov = ws[8];
+    pre_b = -1;
     if (chunk > 0) {
       t_begin = w * chunk;
       t_end = min(t_begin + chunk, total);
-      b = (t_begin < total) ? find_sequence(ws + kWsHeader, B, t_begin) : B;
+      if (has_first) {
+        pre_b = f0;
+        pre_c0 = f1;
+        pre_c1 = f2;
+        pre_len = f3;
+        b = pre_b;
+      } else {
+        b = (t_begin < total) ? find_sequence(ws + kWsCu, B, t_begin) : B;
+      }
     } else {
       b = w;  // one whole sequence per step, stride = groups
     }
@@ -177,19 +206,29 @@ struct SegmentWalker {
 
   // Returns false when the workgroup has no more work.
   __device__ __forceinline__ bool next(Segment& s) {
-    const int32_t* cu = ws + kWsHeader;
-    const int32_t* len = ws + kWsHeader + B + 1;
+    const int32_t* cu = ws + kWsCu;
+    const int32_t* len = ws + kWsCu + B + 1;
     if (chunk > 0) {
-      // skip sequences that end before the range (empty ones included)
-      while (b < B && cu[b + 1] <= t_begin) ++b;
+      int c0, c1, lb;
+      if (b == pre_b) {
+        // the planner's first segment: empty sequences already skipped
+        c0 = pre_c0;
+        c1 = pre_c1;
+        lb = pre_len;
+      } else {
+        // skip sequences that end before the range (empty ones included)
+        while (b < B && cu[b + 1] <= t_begin) ++b;
+        c0 = (b < B) ? cu[b] : 0;
+        c1 = (b < B) ? cu[b + 1] : 0;
+        lb = (b < B) ? len[b] : 0;
+      }
       if (b >= B || t_begin >= t_end) return false;
-      const int c1 = cu[b + 1];
-      const int rs = cu[b] + ov;  // first real tile of b (b is not empty here)
+      const int rs = c0 + ov;  // first real tile of b (b is not empty here)
       if (rs >= t_end) return false;
       const int lo = max(t_begin, rs), hi = min(t_end, c1);
       s.b = b;
       s.tok_begin = (lo - rs) * kPlanTile;
-      s.tok_end = min((hi - rs) * kPlanTile, len[b]);
+      s.tok_end = min((hi - rs) * kPlanTile, lb);
       const int first = rs / chunk;
       s.split = w - first;
       s.nsplits = (c1 - 1) / chunk - first + 1;
@@ -223,7 +262,7 @@ __device__ __forceinline__ int xcd_local_index(int p, int grid) {
 // the threads of the workgroup split the (sequence, row) pairs between them.
 __device__ __forceinline__ void mark_empty_sequences(const DecodeArgs& a, int tid, int nthreads) {
   if (a.ws[7] == 0) return;
-  const int32_t* len = a.ws + kWsHeader + a.B + 1;
+  const int32_t* len = a.ws + kWsCu + a.B + 1;
   const int R = a.Lq * a.H;
   for (int i = tid; i < a.B * R; i += nthreads) {
     const int b = i / R;

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
   const int jq = row_ok ? n / a.H : 0;
   const int hi = lane >> 5;
   const int S = a.splits;
-  const int32_t* len = ws + kWsHeader + a.B + 1;
+  const int32_t* len = ws + kWsCu + a.B + 1;
   // a schedule planned for another batch (or head grouping) is never walked
   if (ws[6] != a.B) return;
 
@@ -327,8 +327,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
       }
     };
 
+    // With 32 rows or fewer (RG = 1) all four waves need the same query rows:
+    // instead of four loads of the same 37 KB, the block is copied once into
+    // the fourth ring stage (free until sub-tile 3 is copied, after the first
+    // loop barrier) with the sub-tile layout, and every wave reads its
+    // operands from there, as it reads cache rows.
+    constexpr bool kQLds = !F8 && RG == 1;
     bf16x8 q[kKSteps];
-    {
+    if constexpr (!kQLds) {
       const uint16_t* qrow = qc + ((size_t)b * R + (row_ok ? n : 0)) * kD + 8 * hi;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks)
@@ -338,10 +344,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
     // [next window]; the first copy needs this window
     const int tv_next = have_next ? table_window(nseg) : 0;
     if (first_seg) {
-      if (have_next) vm_wait<kKSteps + 1>();
-      else vm_wait<kKSteps>();
+      constexpr int kQLoads = kQLds ? 0 : kKSteps;
+      if (have_next) vm_wait<kQLoads + 1>();
+      else vm_wait<kQLoads>();
       first_seg = false;
     }
+    // source offset of this lane's part of query-block copy piece i: the
+    // sub-tile layout over rows 0 .. 31 of the sequence, rows past R
+    // repeating row R - 1 (never read past the sequence's rows)
+    auto q_src = [&](int i) {
+      const int qq = q_lane + 256 * i;
+      const int r = (qq * 1821) >> 17;  // qq / 72
+      const int pc = qq - r * kChunks;
+      return min(r, R - 1) * kRowBytes + ((pc ^ swz(r)) << 4);
+    };
 
     const float qk_scale = a.scale * (F8 ? a.kv_scale : 1.f) * kLog2e;
     const int lim_row = row_ok ? min(seg.tok_end, L - a.Lq + jq + 1) : 0;
@@ -372,6 +388,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         // copies issued after any sub-tile is then the same constant
 #pragma unroll
         for (int s2 = 0; s2 < kF8Ahead; ++s2) issue_or_sink(s2);
+      } else if (kQLds && pass == 0) {
+        // sub-tile 0, the query block, then sub-tiles 1 and 2: the wait for
+        // sub-tile 0 below also covers the query block
+        issue(0);
+        const uint8_t* qbase = reinterpret_cast<const uint8_t*>(qc + (size_t)b * R * kD);
+#pragma unroll
+        for (int i = 0; i < kDmaN; ++i) dma_at(qbase, stage_addr(3) + wave * 1024, 4096u, i, q_src(i));
+        for (int s2 = 1; s2 < min(3, n_sub); ++s2) issue(s2);
       } else {
         for (int s2 = 0; s2 < min(3, n_sub); ++s2) issue(s2);
       }
@@ -408,6 +432,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_mfma_kernel(DecodeArgs a, 
         vm_wait_tiles<kDmaN>(min(2, n_sub - 1));
         block_sync();
         fix_partial(0);
+        if constexpr (kQLds) {
+          if (pass == 0) {
+            int kq[4];
+            kbases(3, kq);
+#pragma unroll
+            for (int ks = 0; ks < kKSteps; ++ks) q[ks] = kload(kq, ks);
+          }
+        }
       }
       f32x16 sc;
       if constexpr (F8) {

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic(DecodeArgs a) {
   const T* qc = (const T*)a.q_cat;
   const C* cache = (const C*)a.cache;
   const float kv = kF8 ? a.kv_scale : 1.f;
-  const int32_t* len = a.ws + kWsHeader + a.B + 1;
+  const int32_t* len = a.ws + kWsCu + a.B + 1;
   // a schedule planned for another batch (or head grouping) is never walked
   if (a.ws[6] != a.B) return;
 

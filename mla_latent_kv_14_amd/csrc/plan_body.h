@@ -68,8 +68,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
   int32_t* ws = pa.ws;
   if (threadIdx.x == 0) sh.bad = 0x7fffffff;
   __syncthreads();
-  int32_t* cu = ws + kWsHeader;
-  int32_t* len = ws + kWsHeader + B + 1;
+  int32_t* cu = ws + kWsCu;
+  int32_t* len = ws + kWsCu + B + 1;
 
   int local_sum = 0, local_max = 0, local_empty = 0;
   for (int b = threadIdx.x; b < B; b += kPlanThreads) {
@@ -129,6 +129,22 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
     ws[8] = pa.ov;
     ws[9] = pa.hg_log2;
     for (int k = 10; k < kWsHeader; ++k) ws[k] = 0;
+  }
+  // each workgroup's first segment (chunked mode): the sequence that holds
+  // line tile w * chunk, past any sequence that ends at or before it, with
+  // its cu and length words
+  __syncthreads();
+  if (chunk > 0) {
+    for (int w = threadIdx.x; w < min(groups, kFirstMax); w += kPlanThreads) {
+      const int t = w * chunk;
+      int b = (t < offset) ? find_sequence(cu, B, t) : B;
+      while (b < B && cu[b + 1] <= t) ++b;
+      int32_t* f = ws + kWsHeader + 4 * w;
+      f[0] = b;
+      f[1] = (b < B) ? cu[b] : 0;
+      f[2] = (b < B) ? cu[b + 1] : 0;
+      f[3] = (b < B) ? len[b] : 0;
+    }
   }
 }
 

@@ -69,6 +69,7 @@ PLAN_TILE = 64
 
 
 WS_HEADER = 16
+WS_CU = WS_HEADER + 4 * 1024  # the per-workgroup first-segment words come first
 
 
 def replay_schedule(ws: np.ndarray):
@@ -85,8 +86,8 @@ def replay_schedule(ws: np.ndarray):
     segments (w, b, tok_begin, tok_end, split, nsplits, g), lengths per sequence).
     """
     chunk, groups, total, maxn, splits, err, B, empty, ov, hgl = (int(x) for x in ws[:10])
-    cu = ws[WS_HEADER:WS_HEADER + B + 1].astype(np.int64)
-    lens = ws[WS_HEADER + B + 1:WS_HEADER + 2 * B + 1].astype(np.int64)
+    cu = ws[WS_CU:WS_CU + B + 1].astype(np.int64)
+    lens = ws[WS_CU + B + 1:WS_CU + 2 * B + 1].astype(np.int64)
     segs = []
     if chunk > 0:
         for w in range(groups):
@@ -104,6 +105,15 @@ def replay_schedule(ws: np.ndarray):
     else:
         for b in range(B):
             segs.append((b % groups, b >> hgl, 0, int(lens[b]), 0, 1, b & ((1 << hgl) - 1)))
+    if chunk > 0:  # each workgroup's first segment, as the planner precomputes it for the attention kernels
+        for w in range(min(groups, 1024)):
+            t = w * chunk
+            b = int(np.searchsorted(cu, t, side="right")) - 1 if t < total else B
+            while b < B and cu[b + 1] <= t:
+                b += 1
+            want = (b, int(cu[b]), int(cu[b + 1]), int(lens[b])) if b < B else (B, 0, 0, 0)
+            got = tuple(int(x) for x in ws[WS_HEADER + 4 * w:WS_HEADER + 4 * w + 4])
+            assert got == want, f"first segment of workgroup {w}: {got} != {want}"
     hdr = dict(chunk=chunk, groups=groups, total=total, maxn=maxn, splits=splits, error=err, B=B >> hgl,
                empty=empty, ov=ov, hg=1 << hgl)
     return hdr, segs, lens[::1 << hgl]
