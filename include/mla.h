@@ -168,7 +168,8 @@ int mla_decode(const mla_dims* dims, const void* q_cat, const void* kv_cache, co
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same planner and attention kernels, with the work schedule kept in a
  * library-owned device array instead of a caller workspace.  The array holds
- * the schedule of up to 65536 sequences (about 512 KiB); each GPU the library
+ * the schedule of up to 65536 sequences (about 528 KiB; with head groups,
+ * see mla_decode, each group counts as a sequence); each GPU the library
  * runs on keeps its own copy until the process ends.  Arguments and results
  * are those of mla_decode without workspace/workspace_bytes.  The call
  * allocates nothing.  MLA_ERR_WORKSPACE when dims->batch > 65536; the other
