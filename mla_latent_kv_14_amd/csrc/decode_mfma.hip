@@ -9,7 +9,11 @@
 // Multi-Head Latent Attention Guide", section 4: latents and RoPE keys loaded
 // once into on-chip memory, scores and latent-weighted sums in one pass).
 // Four sub-tile buffers (144 KiB) keep three sub-tiles in flight while one is
-// computed.
+// computed.  With 32 query rows or fewer the four waves share the rows and
+// split the output columns; their common query block is then copied once per
+// piece into the fourth buffer (free until sub-tile 3) and read from there.
+// With head groups (DecodeArgs::hg_log2) a scheduled "sequence" is one group
+// of heads of a real sequence, whose block-table row it reads.
 //
 // Per sub-tile and wave (32 query rows):
 //   S^T[token, row] = K[token, 0:576] . q_cat[row, 0:576]   36 MFMA 32x32x16
@@ -46,7 +50,8 @@
 // the row, so every 1 KiB copy reads 16 contiguous 64-byte row segments and
 // neither operand read has LDS bank conflicts: the score operand (8 codes of
 // one row) is a ds_read_b64, and the latent-sum operand (8 tokens of one
-// column) a ds_read_b64_tr_b8, the 8-bit transpose read.  Each operand is converted to bf16 in registers right before its
+// column) a ds_read_b64_tr_b8, the 8-bit transpose read.  Each operand is
+// converted to bf16 in registers right before its
 // MFMA (E4M3 values are exact in bf16, so the matrix products see exactly
 // the cached values and run in the same order as on a bf16 cache), and
 // nothing but the codes ever goes through LDS.  Rows past the range are
