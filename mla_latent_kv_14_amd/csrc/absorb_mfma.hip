@@ -161,6 +161,10 @@ __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __rest
 // Every output element takes the same chain either way, and both kernels
 // that apply W_UV use this, so they round identically.
 constexpr int kThreadsC = 512;
+// merge: partials of a group's first two splits are requested before their
+// weights are known (two measured faster than one, three or four: a split
+// requested for nothing still costs its bytes)
+constexpr int kSpecSplits = 2;
 
 struct WuvOperands {
   uint4 bw[kDC / 32];
@@ -295,48 +299,69 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
   const int r = g >> lgP, p = g & (P - 1), m = m0 + r;
   const bool valid = r < rows;
 
-  // Loads complete in issue order, so the row's first split lse values are
-  // requested before anything else: waiting for them (and for the first
-  // chunk of partials) never waits for the W_UV rows, which are requested
-  // after that chunk and are needed only by the product.
+  // Loads complete in issue order.  The row's first sixteen split lse values
+  // are requested first, then the partials of the group's first kSpecSplits
+  // splits (before their weights are known: every split index below S is in
+  // bounds, and a split whose weight turns out zero is simply not used), then
+  // the rest of the first chunk and the W_UV rows.  So the wait for the lse
+  // values waits for nothing else, the first partials travel during that
+  // wait, and only the later chunks' waits include the W_UV rows, which the
+  // product needs last.
   const float* lp = lse_part + ((size_t)(valid ? m : m0) * H + h) * S;
   const float lfirst = (valid && j8 < S) ? lp[j8] : -INFINITY;
+  const float lsecond = (valid && j8 + 8 < S) ? lp[j8 + 8] : -INFINITY;
+  // bf16 partials: four columns (8 bytes) per load
+  const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)(valid ? m : m0) * H + h) * S * kDC) + j;
+  // The group's splits in merge order, four at a time: chunk c covers splits
+  // s0 .. s0 + 3 of block p + P (c >> 1), s0 = 8 (p + P (c >> 1)) + 4 (c & 1).
+  auto chunk_start = [&](int c) { return kMergeBlock * (p + P * (c >> 1)) + 4 * (c & 1); };
+  uint2 x[4][8];
+  const int s00 = chunk_start(0);
+  if (valid) {
+#pragma unroll
+    for (int u = 0; u < kSpecSplits; ++u)
+      if (s00 + u < S) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[u][k] = src[(size_t)(s00 + u) * (kDC / 4) + 16 * k];
+      }
+  }
   float total = -INFINITY;
   if (valid) {
-    total = split_lse_first(lfirst, lp, S, j8);
+    total = split_lse_first2(lfirst, lsecond, lp, S, j8);
     if (lse_out != nullptr && p == 0 && j == 0 && blockIdx.z == 0) lse_out[(size_t)m * H + h] = total;
   }
 
   float4 acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  // bf16 partials: four columns (8 bytes) per load
-  const uint2* src = reinterpret_cast<const uint2*>(o_part + ((size_t)(valid ? m : m0) * H + h) * S * kDC) + j;
-  auto fma4 = [&](float wgt, const uint2* x) {
+  auto fma4 = [&](float wgt, const uint2* xx) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      acc[k].x = fmaf(wgt, __uint_as_float(x[k].x << 16), acc[k].x);
-      acc[k].y = fmaf(wgt, __uint_as_float(x[k].x & 0xffff0000u), acc[k].y);
-      acc[k].z = fmaf(wgt, __uint_as_float(x[k].y << 16), acc[k].z);
-      acc[k].w = fmaf(wgt, __uint_as_float(x[k].y & 0xffff0000u), acc[k].w);
+      acc[k].x = fmaf(wgt, __uint_as_float(xx[k].x << 16), acc[k].x);
+      acc[k].y = fmaf(wgt, __uint_as_float(xx[k].x & 0xffff0000u), acc[k].y);
+      acc[k].z = fmaf(wgt, __uint_as_float(xx[k].y << 16), acc[k].z);
+      acc[k].w = fmaf(wgt, __uint_as_float(xx[k].y & 0xffff0000u), acc[k].w);
     }
   };
-  // The group's splits in merge order, four at a time: chunk c covers splits
-  // s0 .. s0 + 3 of block p + P (c >> 1), s0 = 8 (p + P (c >> 1)) + 4 (c & 1).
-  // Splits of block 0 take their lse from the lanes that loaded it; splits
-  // with lse_s = -inf are skipped (their o_s is never read).
-  auto chunk_start = [&](int c) { return kMergeBlock * (p + P * (c >> 1)) + 4 * (c & 1); };
-  auto load_chunk = [&](int s0, float* wv, uint2 (*x)[8]) {
+  // Weights of chunk s0 .. s0 + 3; splits of blocks 0 and 1 take their lse
+  // from the lanes that loaded it.  Splits with lse_s = -inf get weight 0 and
+  // are skipped (their o_s is never used).
+  auto weights = [&](int s0, float* wv) {
     float ls[4];
     if (s0 < kMergeBlock) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) ls[u] = __shfl(lfirst, (lane & ~7) | (s0 + u), 64);
+    } else if (s0 < 2 * kMergeBlock) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ls[u] = __shfl(lsecond, (lane & ~7) | (s0 - kMergeBlock + u), 64);
     } else {
 #pragma unroll
       for (int u = 0; u < 4; ++u) ls[u] = (s0 + u < S) ? lp[s0 + u] : -INFINITY;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) wv[u] = (s0 + u >= S || ls[u] == -INFINITY) ? 0.f : expf(ls[u] - total);
+  };
+  auto load_chunk = [&](int s0, const float* wv) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (wv[u] != 0.f) {
@@ -344,23 +369,32 @@ __global__ __launch_bounds__(kThreadsC) void combine_out_mfma(const uint16_t* __
         for (int k = 0; k < 8; ++k) x[u][k] = src[(size_t)(s0 + u) * (kDC / 4) + 16 * k];
       }
   };
-  auto merge_chunk = [&](const float* wv, uint2 (*x)[8]) {
+  auto merge_chunk = [&](const float* wv) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (wv[u] != 0.f) fma4(wv[u], x[u]);
   };
   float wv[4];
-  uint2 x[4][8];
-  const bool first_chunk = valid && chunk_start(0) < S;
-  if (first_chunk) load_chunk(chunk_start(0), wv, x);
+  const bool first_chunk = valid && s00 < S;
+  if (first_chunk) {
+    weights(s00, wv);
+    // splits the speculative loads did not cover
+#pragma unroll
+    for (int u = kSpecSplits; u < 4; ++u)
+      if (wv[u] != 0.f) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[u][k] = src[(size_t)(s00 + u) * (kDC / 4) + 16 * k];
+      }
+  }
   WuvOperands op;
   const WuvRole ro = wuv_role(wave, (int)gridDim.z, (int)blockIdx.z);
   wuv_request(w_uv, h, ro, lane, op);
   if (first_chunk) {
-    merge_chunk(wv, x);
+    merge_chunk(wv);
     for (int c = 1; chunk_start(c) < S; ++c) {
-      load_chunk(chunk_start(c), wv, x);
-      merge_chunk(wv, x);
+      weights(chunk_start(c), wv);
+      load_chunk(chunk_start(c), wv);
+      merge_chunk(wv);
     }
   }
   // float4 column block k of thread j is columns 4 (j + 16 k) .. + 3

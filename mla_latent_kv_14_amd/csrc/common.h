@@ -133,6 +133,22 @@ __device__ __forceinline__ float split_lse_first(float first, const float* lp, i
   for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off, 64);
   return mx + logf(z);
 }
+// The same with the lane's second value lp[j + 8] (-inf if j + 8 >= S) also
+// loaded by the caller: the same maximum and the same sum, in the same order.
+__device__ __forceinline__ float split_lse_first2(float first, float second, const float* lp, int S, int j) {
+  float mx = fmaxf(fmaxf(-INFINITY, first), second);
+  for (int s = j + 16; s < S; s += 8) mx = fmaxf(mx, lp[s]);
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (mx == -INFINITY) return -INFINITY;
+  float z = 0.f;
+  if (j < S) z += expf(first - mx);
+  if (j + 8 < S) z += expf(second - mx);
+  for (int s = j + 16; s < S; s += 8) z += expf(lp[s] - mx);
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) z += __shfl_xor(z, off, 64);
+  return mx + logf(z);
+}
 __device__ __forceinline__ float split_lse(const float* lp, int S, int j) {
   return split_lse_first(j < S ? lp[j] : -INFINITY, lp, S, j);
 }
