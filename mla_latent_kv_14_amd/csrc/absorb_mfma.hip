@@ -30,7 +30,7 @@ constexpr int kDC = 512;   // d_c
 constexpr int kNQ = 128;   // absorb_q: columns of q~ per workgroup
 
 // ------------------------------------------------------------------ absorb_q
-// grid (H, d_c / 128, ceil(M / 64)): workgroup (h, nq, mt) computes columns
+// 4 H ceil(M / 64) workgroups; workgroup (h, nq, mt) computes columns
 // 128 nq .. 128 nq + 127 of q~ for rows 64 mt .. 64 mt + 63; wave w takes the
 // 32 columns 32 w .. 32 w + 31 of that quarter.  The W quarter and the 64
 // q_nope rows are both staged in LDS once per workgroup.  The MFMA computes q~^T =
@@ -39,22 +39,27 @@ constexpr int kNQ = 128;   // absorb_q: columns of q~ per workgroup
 // and stores them as one 8-byte write.
 constexpr int kRowsQ = 64;  // rows of q_nope per workgroup (two 32-row MFMA tiles)
 
-// With a plan (launched with one more x slice), workgroup (H, 0, 0) runs the
-// decode planner (plan_body.h) on the lengths instead, so the step's schedule
-// costs no launch of its own; the rest of that slice does nothing.
+// The grid is one-dimensional: with a plan, workgroup 0 runs the decode
+// planner (plan_body.h) on the lengths, so the step's schedule costs no
+// launch of its own, and it starts first, since with few rows it is the
+// longest.  The others are w = e + h + H (nq + 4 mt), e = 1 with a plan and
+// 0 without, so with H a multiple of 8 the four quarters of one head share an
+// XCD (and the L2 that holds their q_nope rows).
 __global__ __launch_bounds__(kThreads) void absorb_q_mfma(const uint16_t* __restrict__ q_nope,
                                                           const uint16_t* __restrict__ q_rope,
                                                           const uint16_t* __restrict__ w_uk,
                                                           uint16_t* __restrict__ q_cat, int M, int H, int d_r,
                                                           PlanArgs pa) {
-  if ((int)blockIdx.x == H) {
+  const bool with_plan = pa.ws != nullptr;  // launched with a plan: its workspace is never null
+  if (with_plan && blockIdx.x == 0) {
     __shared__ PlanShared psh;
-    if (blockIdx.y == 0 && blockIdx.z == 0) plan_body(pa, psh);
+    plan_body(pa, psh);
     return;
   }
+  const int wid = (int)blockIdx.x - (with_plan ? 1 : 0);
   // W quarter: row k (0..127) holds 16 chunks of 16 B; chunk c sits at c ^ (4 * (k & 3))
   __shared__ __attribute__((aligned(16))) uint8_t wt[kDN * kNQ * 2];
-  const int h = blockIdx.x, nq = blockIdx.y, mbase = blockIdx.z * kRowsQ;
+  const int h = wid % H, nq = (wid / H) % (kDC / kNQ), mbase = (wid / (H * (kDC / kNQ))) * kRowsQ;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5;
   const int D = kDC + d_r;
 
@@ -443,8 +448,8 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, const void* q_nope, const voi
   const int M = d.batch * d.q_len;
   PlanArgs pa{};
   if (plan != nullptr) pa = *plan;
-  hipLaunchKernelGGL(absorb_q_mfma, dim3(d.num_heads + (plan != nullptr ? 1 : 0), kDC / kNQ, (M + kRowsQ - 1) / kRowsQ),
-                     dim3(kThreads), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
+  const int grid = d.num_heads * (kDC / kNQ) * ((M + kRowsQ - 1) / kRowsQ) + (plan != nullptr ? 1 : 0);
+  hipLaunchKernelGGL(absorb_q_mfma, dim3(grid), dim3(kThreads), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_rope, (const uint16_t*)w_uk,
                      (uint16_t*)q_cat, M, d.num_heads, d.d_rope, pa);
   return hipGetLastError();
 }

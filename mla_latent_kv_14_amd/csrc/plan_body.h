@@ -34,33 +34,40 @@ inline PlanArgs make_plan_args(const mla_dims& d, const int32_t* seq_lens, int s
 }
 
 struct PlanShared {
-  int red[kPlanThreads / 64];
-  int scan[kPlanThreads];
+  int red[kPlanThreads / 64][3];
+  int wsum[kPlanThreads / 64];
   int bad;
+  // with B <= kPlanThreads: the prefix sums and lengths, so that the
+  // first-segment searches read LDS instead of waiting on global memory
+  int cu[kPlanThreads + 1];
+  int len[kPlanThreads];
 };
 
-__device__ __forceinline__ int plan_reduce_sum(int v, int* red) {
+// Sum of a, maximum of b and sum of c over the workgroup, with one pair of
+// barriers (integer arithmetic: the order does not matter).
+__device__ __forceinline__ void plan_reduce3(int& a, int& b, int& c, int (*red)[3]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 32; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b = max(b, __shfl_xor(b, off, 64));
+    c += __shfl_xor(c, off, 64);
+  }
   __syncthreads();
-  if (lane == 0) red[wave] = v;
+  if (lane == 0) {
+    red[wave][0] = a;
+    red[wave][1] = b;
+    red[wave][2] = c;
+  }
   __syncthreads();
-  int t = 0;
-  for (int i = 0; i < kPlanThreads / 64; ++i) t += red[i];
-  return t;
-}
-
-__device__ __forceinline__ int plan_reduce_max(int v, int* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  int t = red[0];
-  for (int i = 1; i < kPlanThreads / 64; ++i) t = max(t, red[i]);
-  return t;
+  a = red[0][0];
+  b = red[0][1];
+  c = red[0][2];
+  for (int i = 1; i < kPlanThreads / 64; ++i) {
+    a += red[i][0];
+    b = max(b, red[i][1]);
+    c += red[i][2];
+  }
 }
 
 __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
@@ -71,20 +78,22 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
   int32_t* cu = ws + kWsCu;
   int32_t* len = ws + kWsCu + B + 1;
 
-  int local_sum = 0, local_max = 0, local_empty = 0;
+  const bool small = B <= kPlanThreads;  // one sequence per thread: everything stays on chip
+  int local_sum = 0, local_max = 0, local_empty = 0, mine = 0;
   for (int b = threadIdx.x; b < B; b += kPlanThreads) {
     int L = pa.seq_lens[b >> pa.hg_log2];
     if (L < pa.q_len || L > pa.max_len) atomicMin(&sh.bad, b >> pa.hg_log2);
     L = min(max(L, 0), pa.max_len);
     len[b] = L;
+    mine = L;
+    if (small) sh.len[b] = L;
     const int n = (L + kPlanTile - 1) / kPlanTile;
     local_sum += n + (n > 0 ? pa.ov : 0);
     local_max = max(local_max, n);
     local_empty += (L == 0);
   }
-  const int total = plan_reduce_sum(local_sum, sh.red);
-  const int maxn = plan_reduce_max(local_max, sh.red);
-  const int empty = plan_reduce_sum(local_empty, sh.red);
+  plan_reduce3(local_sum, local_max, local_empty, sh.red);
+  const int total = local_sum, maxn = local_max, empty = local_empty;
 
   int chunk, groups;
   if (pa.splits == 1) {
@@ -101,20 +110,31 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
   int offset = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int b = base + threadIdx.x;
-    int n = (b < B) ? (len[b] + kPlanTile - 1) / kPlanTile : 0;
+    int n = (b < B) ? ((small ? mine : len[b]) + kPlanTile - 1) / kPlanTile : 0;
     n += (n > 0) ? pa.ov : 0;
-    __syncthreads();
-    sh.scan[threadIdx.x] = n;
-    __syncthreads();
-    for (int d = 1; d < kPlanThreads; d <<= 1) {
-      const int add = (threadIdx.x >= d) ? sh.scan[threadIdx.x - d] : 0;
-      __syncthreads();
-      sh.scan[threadIdx.x] += add;
-      __syncthreads();
+    // inclusive scan within the wave by shuffles, then the waves' totals
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int v = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(v, d, 64);
+      if (lane >= d) v += y;
     }
-    if (b < B) cu[b] = offset + sh.scan[threadIdx.x] - n;
-    offset += sh.scan[kPlanThreads - 1];
+    __syncthreads();  // the previous window's totals have been read
+    if (lane == 63) sh.wsum[wave] = v;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int i = 0; i < kPlanThreads / 64; ++i) {
+      before += (i < wave) ? sh.wsum[i] : 0;
+      all += sh.wsum[i];
+    }
+    if (b < B) {
+      cu[b] = offset + before + v - n;
+      if (small) sh.cu[b] = offset + before + v - n;
+    }
+    offset += all;
   }
+  if (small && threadIdx.x == 0) sh.cu[B] = offset;
   __syncthreads();
   if (threadIdx.x == 0) {
     cu[B] = offset;
@@ -135,15 +155,17 @@ __device__ __forceinline__ void plan_body(const PlanArgs& pa, PlanShared& sh) {
   // its cu and length words
   __syncthreads();
   if (chunk > 0) {
+    const int32_t* cs = small ? sh.cu : cu;
+    const int32_t* ls = small ? sh.len : len;
     for (int w = threadIdx.x; w < min(groups, kFirstMax); w += kPlanThreads) {
       const int t = w * chunk;
-      int b = (t < offset) ? find_sequence(cu, B, t) : B;
-      while (b < B && cu[b + 1] <= t) ++b;
+      int b = (t < offset) ? find_sequence(cs, B, t) : B;
+      while (b < B && cs[b + 1] <= t) ++b;
       int32_t* f = ws + kWsHeader + 4 * w;
       f[0] = b;
-      f[1] = (b < B) ? cu[b] : 0;
-      f[2] = (b < B) ? cu[b + 1] : 0;
-      f[3] = (b < B) ? len[b] : 0;
+      f[1] = (b < B) ? cs[b] : 0;
+      f[2] = (b < B) ? cs[b + 1] : 0;
+      f[3] = (b < B) ? ls[b] : 0;
     }
   }
 }
