@@ -88,6 +88,10 @@ def replay_schedule(ws: np.ndarray):
     chunk, groups, total, maxn, splits, err, B, empty, ov, hgl = (int(x) for x in ws[:10])
     cu = ws[WS_CU:WS_CU + B + 1].astype(np.int64)
     lens = ws[WS_CU + B + 1:WS_CU + 2 * B + 1].astype(np.int64)
+    # the line: entry b takes ceil(len / tile) real tiles, plus ov when it has any
+    n = -(-lens // PLAN_TILE)
+    n = n + np.where(n > 0, ov, 0)
+    assert cu[0] == 0 and np.array_equal(np.diff(cu), n) and cu[B] == total, "schedule prefix sums"
     segs = []
     if chunk > 0:
         for w in range(groups):

@@ -119,6 +119,24 @@ def test_split_sweep(splits):
             assert len(pieces) == pieces[0][3] <= r.num_splits
 
 
+@pytest.mark.parametrize("batch", [256, 257, 600])
+def test_many_sequences(batch):
+    """More sequences than the planner has threads: its prefix sum runs over
+    several windows and its searches read the sums from the workspace.  Every
+    element against the oracle, and the schedule's sums against the lengths."""
+    rng = np.random.default_rng(batch)
+    lens = tuple(int(x) for x in rng.integers(1, 200, size=batch))
+    wl = workload("mtp2_lognormal_bf16", batch=batch, q_len=1, lengths=("fixed", lens))
+    r = _full_check(make_problem(wl, 17), check_intermediate=False)
+    hdr, segs, got = replay_schedule(r.workspace.cpu().numpy())
+    assert hdr["B"] == batch and hdr["error"] == 0
+    assert np.array_equal(got, r.prob.seq_lens)
+    covered = {}
+    for (_, b, t0, t1, _, _, _) in segs:
+        covered[b] = covered.get(b, 0) + (t1 - t0)
+    assert covered == {b: int(L) for b, L in enumerate(r.prob.seq_lens)}
+
+
 def test_block_permutation_bit_identical():
     wl = workload("single_4k_bf16", batch=3, lengths=("fixed", (700, 129, 1500)))
     p = make_problem(wl, 31)
